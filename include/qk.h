@@ -1,0 +1,245 @@
+/*
+ * qk.h - C interface of libqk, the MI355X (gfx950) library for the forward
+ * pass of a LLaMA-architecture decoder layer over 4-bit block-quantized
+ * weights (Q4_0) and 8-bit block-quantized activations (Q8_0).
+ *
+ * Sources, cited by page title and section:
+ *  [GUIDE]    kenji.blog, "Guide to developing small-scale AI models (such as
+ *             TinyLLaMA) with C++": 2 pipeline figure, 4.1 RMSNorm, 4.2 RoPE,
+ *             4.3 GQA, 4.4 SwiGLU, 5.1 arena allocation, 5.2 per-step graph
+ *             figure, 6.1 block quantization, 7 KV cache.
+ *  [LLAMACPP] kenji.blog, "Guide to using llama.cpp and customizing it with
+ *             C++": 2.1 (decode is a GEMV), 2.2 block quantization equations.
+ *  [ENGINE]   kenji.blog, "No Python needed: an AI inference engine in C++
+ *             only": 6 GEMM, 7.1 backend interface, 8 attention and KV cache.
+ *  [COLIBRI]  kerneldigest.dev, "Colibri: running 744B MoE models on consumer
+ *             hardware by streaming experts": System architecture, token flow.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *    the comment says "host".  Outputs are caller-allocated
+ *    (out-parameter style, as in the backend interface of [ENGINE 7.1]).
+ *  - Calls enqueue work on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and return without synchronizing.  Buffers must stay
+ *    alive until the stream has finished.  No call allocates or frees device
+ *    memory: scratch space is a caller workspace `ws` of `ws_bytes` bytes
+ *    whose size the matching qk_*_workspace() query returns (the arena
+ *    principle of [GUIDE 5.1]: nothing is allocated inside the loop).
+ *  - Return value: QK_OK (0) on success, a negative QK_E* code otherwise.
+ *    Arguments are validated on the host before anything is enqueued; on a
+ *    validation error nothing is enqueued and outputs are untouched.
+ *    QK_EHIP reports a launch failure from the HIP runtime.
+ *  - Layouts are row-major.  fp16 values travel as uint16_t bit patterns
+ *    (IEEE binary16).
+ *  - Q4_0 weights [n][k] (k % 32 == 0) are stored split:
+ *      w_q : uint8 [n][k/2], 16 bytes per 32-element block; byte j of a block
+ *            holds element j in its low nibble and element j+16 in its high
+ *            nibble; a nibble c encodes the integer c - 8 (c in [0, 15]);
+ *      w_d : fp16 [n][k/32], the block scales.
+ *    Weight value = w_d * (c - 8) [LLAMACPP 2.2; GUIDE 6.1].  w_q must be
+ *    16-byte aligned.
+ *  - Q8_0 activations [m][k] are stored split: x_q int8 [m][k] (16-byte
+ *    aligned), x_d fp16 [m][k/32].  Value = x_d * x_q.
+ *  - float arrays must be 16-byte aligned.
+ *  - Calls on different streams that touch disjoint buffers may run
+ *    concurrently; calls that share a workspace must be ordered.
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QK_OK 0
+#define QK_EINVAL (-1)     /* null pointer or out-of-range value */
+#define QK_ESHAPE (-2)     /* k % 32 != 0, nq % nkv != 0, odd head_dim, ... */
+#define QK_EALIGN (-3)     /* a pointer is not aligned as documented */
+#define QK_EWORKSPACE (-4) /* workspace missing or smaller than required */
+#define QK_EHIP (-5)       /* the HIP runtime reported an error */
+
+/* Text for a status code (static storage, never NULL). */
+const char* qk_strerror(int status);
+
+/* ---------------------------------------------------------------------- */
+/* Quantization                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* Q8_0 quantization of activations [LLAMACPP 2.2: the input vector is
+ * block-quantized like the weights; COLIBRI: int8 activations].  For each
+ * block of 32 values of each row: d = max|x| / 127 in fp32 (IEEE division),
+ * q = round-half-away-from-zero(x / d) clamped to [-127, 127] (q = 0 when
+ * d == 0), and d is stored as fp16 (round to nearest even).
+ * x [rows][k] fp32 -> x_q int8 [rows][k], x_d fp16 [rows][k/32].
+ * Requires k % 32 == 0.  Bit-exact by contract. */
+int quantize_q8_0(const float* x, int64_t rows, int64_t k, int8_t* x_q, uint16_t* x_d,
+                  void* stream);
+
+/* Q4_0 quantization of weights [LLAMACPP 2.2: delta = max|w| / 7, codes in
+ * [-8, 7]; GUIDE 6.1: 32 values per block, fp16 scale].  Per block:
+ * delta = max|w| / 7 in fp32, c = round-half-away-from-zero(w / delta)
+ * clamped to [-8, 7], nibble = c + 8 (8 for an all-zero block), delta stored
+ * as fp16.  w [n][k] fp32 -> w_q [n][k/2], w_d [n][k/32].  Bit-exact. */
+int qk_quantize_q4_0(const float* w, int64_t n, int64_t k, uint8_t* w_q, uint16_t* w_d,
+                     void* stream);
+
+/* Host helper: convert Q4_0 from interleaved 18-byte blocks (fp16 scale,
+ * then 16 nibble bytes; [n][k/32] blocks, host memory) to the split layout
+ * (host memory).  Returns QK_ESHAPE when k % 32 != 0. */
+int qk_q4_0_from_blocks(const void* aos18, int64_t n, int64_t k, uint8_t* w_q, uint16_t* w_d);
+
+/* ---------------------------------------------------------------------- */
+/* The quantized matmul                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* y[t][r] = sum_b fp(w_d[r][b]) * fp(x_d[t][b]) * isum[t][r][b], with the
+ * exact int32 block dot isum = sum_{j<32} (c_{r,32b+j} - 8) * x_q[t][32b+j]
+ * [LLAMACPP 2.2: y ~ delta * delta_x * sum q q_x, the integer part being pure
+ * integer arithmetic; ENGINE 6: C = A B].  W [n][k] Q4_0, x [m][k] Q8_0,
+ * y [m][n] fp32 (accumulated in fp32).  m <= 8 runs the decode GEMV, larger
+ * m the int8 MFMA GEMM. */
+int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_t n, int64_t k,
+                      const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y,
+                      void* stream);
+
+/* The per-block int32 dot products themselves, for bit-exact checking:
+ * isum[t][r][b] for t < m, r < n, b < k/32 (int32 [m][n][k/32]). */
+int qk_block_dots_q4_0_q8_0(const uint8_t* w_q, int64_t n, int64_t k, const int8_t* x_q,
+                            int64_t m, int32_t* isum, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Element-wise and normalization ops                                     */
+/* ---------------------------------------------------------------------- */
+
+/* RMSNorm [GUIDE 4.1]: y = x / sqrt(mean(x^2) + eps) * gamma, row by row.
+ * x, y [rows][dim] fp32 (y may equal x), gamma [dim]. */
+int rmsnorm(const float* x, const float* gamma, int64_t rows, int64_t dim, float eps, float* y,
+            void* stream);
+
+/* Interleaved RoPE [GUIDE 4.2], in place: for token t at absolute position
+ * m = pos[t], pair i = (x[2i], x[2i+1]) of every head turns by the angle
+ * m * base^(-2i/head_dim).  x [tokens][heads][head_dim] fp32, pos int32
+ * [tokens] (device).  Requires even head_dim. */
+int rope(float* x, int64_t tokens, int64_t heads, int64_t head_dim, const int32_t* pos,
+         float base, void* stream);
+
+/* SwiGLU [GUIDE 4.4]: h = swish(gate) * up, swish(z) = z / (1 + e^-z).
+ * gate, up, h: n fp32 each. */
+int swiglu(const float* gate, const float* up, int64_t n, float* h, void* stream);
+
+/* KV store [GUIDE 7]: k_cache[seq[t]][g][pos[t]][:] = fp16(k[t][g][:]) and
+ * likewise for v.  k, v [tokens][n_kv][hd] fp32; caches fp16
+ * [seqs][n_kv][cap][hd]; pos, seq int32 [tokens] (device).  pos must be in
+ * [0, cap) and seq must name an existing sequence (not checked on the
+ * device: the caller owns the cache bounds). */
+int qk_kv_append(const float* k, const float* v, int64_t tokens, int64_t n_kv, int64_t hd,
+                 const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,
+                 int64_t cap, void* stream);
+
+/* Embedding lookup [GUIDE 2 figure]: x[i][:] = table[ids[i]][:].
+ * table [vocab][hidden] fp32, ids int32 [n] (device, each in [0, vocab)). */
+int qk_embed_lookup(const float* table, int64_t vocab, int64_t hidden, const int32_t* ids,
+                    int64_t n, float* x, void* stream);
+
+/* Greedy next token [GUIDE 2 figure]: idx[r] = argmax_i logits[r][i], ties
+ * to the lowest index.  logits [rows][vocab] fp32, idx int32 [rows]. */
+int qk_argmax(const float* logits, int64_t rows, int64_t vocab, int32_t* idx, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Attention                                                              */
+/* ---------------------------------------------------------------------- */
+
+/* Grouped-query attention over an fp16 KV cache [ENGINE 8; GUIDE 4.3, 7].
+ * Query head h of token t reads KV head g = h / (n_q_heads / n_kv_heads) of
+ * sequence seq[t] and attends to cache rows 0..pos[t] (inclusive):
+ * s_j = q . k_j / sqrt(head_dim), p = softmax(s), out = sum_j p_j v_j.
+ * q, out [tokens][n_q_heads][head_dim] fp32; caches fp16
+ * [seqs][n_kv_heads][cap][head_dim]; pos, seq int32 [tokens] (device, pos in
+ * [0, cap)).  head_dim must be 32 or 64 and n_q_heads / n_kv_heads at most
+ * 512 / head_dim.  ws: qk_gqa_attention_workspace() bytes. */
+int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads, int64_t n_kv_heads,
+                  int64_t head_dim, const uint16_t* k_cache, const uint16_t* v_cache,
+                  int64_t cap, const int32_t* pos, const int32_t* seq, float* out, void* ws,
+                  size_t ws_bytes, void* stream);
+
+size_t qk_gqa_attention_workspace(int64_t tokens, int64_t n_q_heads, int64_t head_dim,
+                                  int64_t cap);
+
+/* ---------------------------------------------------------------------- */
+/* The decoder layer                                                      */
+/* ---------------------------------------------------------------------- */
+
+typedef struct qk_layer {
+    /* Q4_0 weights, split layout.  w_qkv [(nq + 2 nkv) hd][hidden]: Q rows,
+     * then K rows, then V rows.  w_o [hidden][nq hd].  w_gate_up
+     * [2 ffn][hidden]: the ffn gate rows, then the ffn up rows.
+     * w_down [hidden][ffn]. */
+    const uint8_t* w_qkv_q;
+    const uint16_t* w_qkv_d;
+    const uint8_t* w_o_q;
+    const uint16_t* w_o_d;
+    const uint8_t* w_gate_up_q;
+    const uint16_t* w_gate_up_d;
+    const uint8_t* w_down_q;
+    const uint16_t* w_down_d;
+    const float* gamma_attn; /* [hidden] */
+    const float* gamma_ffn;  /* [hidden] */
+} qk_layer;
+
+typedef struct qk_layer_cfg {
+    int64_t hidden, n_q_heads, n_kv_heads, head_dim;
+    int64_t ffn; /* multiple of 32 (pad with zero rows/columns) */
+    float eps, rope_base;
+    int64_t cap; /* KV cache rows per sequence */
+} qk_layer_cfg;
+
+/* One pre-norm LLaMA decoder layer [GUIDE 5.2 figure; GUIDE 4.1-4.4]:
+ *   u  = rmsnorm(x, gamma_attn); [q|k|v] = w_qkv . Q8_0(u)
+ *   q, k = rope(q, k, pos); k, v -> cache rows pos of seq
+ *   x1 = x + w_o . Q8_0(gqa_attention(q, cache))
+ *   u1 = rmsnorm(x1, gamma_ffn); [g|up] = w_gate_up . Q8_0(u1)
+ *   x2 = x1 + w_down . Q8_0(swiglu(g, up))
+ * x [tokens][hidden] fp32 is updated in place to x2.  Tokens may belong to
+ * different sequences; each token attends causally to rows 0..pos[t] of its
+ * sequence, which includes the rows this call writes.
+ * ws: qk_layer_workspace(cfg, tokens) bytes. */
+int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t tokens,
+                  const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,
+                  void* ws, size_t ws_bytes, void* stream);
+
+size_t qk_layer_workspace(const qk_layer_cfg* cfg, int64_t tokens);
+
+/* ---------------------------------------------------------------------- */
+/* Mixture of experts                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Routed MoE layer [COLIBRI: sigmoid router of the DeepSeek-V3 kind, int8
+ * activation x int4 expert kernels, results combined per token]:
+ *   r = x . w_router (fp32), s = sigmoid(r);
+ *   the top_k experts by s (ties to the lower index; ranked on r itself,
+ *   which orders the same way) with weights s / sum(selected s);
+ *   y_e = down_e . Q8_0(swiglu(gate_e . Q8_0(x), up_e . Q8_0(x)));
+ *   y[t] = sum over ranks 0..top_k-1 of weight * y_e, in rank order.
+ * x [tokens][hidden] fp32; w_router [hidden][n_experts] fp32;
+ * experts stacked: gate_up_q [E][2 ffn][hidden/2], gate_up_d
+ * [E][2 ffn][hidden/32] (gate rows then up rows), down_q [E][hidden][ffn/2],
+ * down_d [E][hidden][ffn/32]; y [tokens][hidden]; sel_idx int32 and sel_w
+ * fp32 [tokens][top_k].  Deterministic: no floating-point atomics.
+ * n_experts <= 1024, top_k <= 32.  ws: qk_moe_workspace() bytes. */
+int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_router,
+                        int64_t n_experts, int32_t top_k, const uint8_t* gate_up_q,
+                        const uint16_t* gate_up_d, const uint8_t* down_q,
+                        const uint16_t* down_d, int64_t ffn, float* y, int32_t* sel_idx,
+                        float* sel_w, void* ws, size_t ws_bytes, void* stream);
+
+size_t qk_moe_workspace(int64_t tokens, int64_t hidden, int64_t n_experts, int32_t top_k,
+                        int64_t ffn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H */

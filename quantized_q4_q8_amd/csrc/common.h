@@ -1,0 +1,80 @@
+// Internal helpers shared by the libqk kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+#include "qk.h"
+
+namespace qk {
+
+constexpr int QBLK = 32;    // values per Q4_0 / Q8_0 block
+constexpr int WAVE = 64;    // CDNA wavefront width
+
+// ---------------------------------------------------------------- fp16 bits
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+// fp32 -> binary16, round to nearest even, subnormals kept (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f2h(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---------------------------------------------------------- wave reductions
+// Butterfly over groups of W adjacent lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// ------------------------------------------------------------ Q8_0 helpers
+// Four adjacent lanes (lane % 4 == 0..3) hold the 32 values of one block,
+// eight consecutive values each.  Computes d = max|x| / 127 (IEEE division)
+// and the eight codes round-half-away-from-zero(v / d) clamped to +-127,
+// packed little-endian into two dwords.  Every lane of the quad gets d.
+__device__ __forceinline__ void q8_quad(const float v[8], uint32_t& lo, uint32_t& hi, float& d) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+    d = amax / 127.0f;
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int q = 0;
+        if (d != 0.0f) {
+            float r = roundf(v[i] / d);
+            r = fminf(127.0f, fmaxf(-127.0f, r));
+            q = (int)r;
+        }
+        b[i] = (uint32_t)(q & 0xFF);
+    }
+    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+}
+
+}  // namespace qk
+
+// ------------------------------------------------------------- host checks
+#define QK_REQUIRE(cond, code) \
+    do {                       \
+        if (!(cond)) return (code); \
+    } while (0)
+
+#define QK_ALIGNED(p, a) ((((uintptr_t)(p)) & ((a)-1)) == 0)
+
+static inline int qk_launch_status() {
+    return hipGetLastError() == hipSuccess ? QK_OK : QK_EHIP;
+}

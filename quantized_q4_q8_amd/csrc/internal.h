@@ -1,0 +1,67 @@
+// Launchers shared between the libqk translation units (host side).
+#pragma once
+
+#include "common.h"
+
+namespace qk {
+
+enum GemvEpilogue : int {
+    EPI_STORE = 0,   // y = acc (+ residual)
+    EPI_SWIGLU = 1,  // rows f and f + ffn are gate and up: y[f] = swish(gate) * up
+};
+
+// A (possibly grouped) Q4_0 x Q8_0 product.  Group g (blockIdx.y) uses the
+// weight matrix at wq + g * wq_gstride (wd + g * wd_gstride) and the
+// activation columns c in [col_off[g], col_off[g+1]) (all m columns when
+// col_off is null).  Column c reads activation row col_idx[c] (c when col_idx
+// is null) and writes output row c: y[c * ldy + row].  With a residual,
+// y[c * ldy + row] = residual[c * ldr + row] + acc (y may equal residual).
+struct GemvArgs {
+    const uint8_t* wq;
+    const uint16_t* wd;
+    int64_t n, k;          // rows (physical) and K of one group's matrix
+    int64_t wq_gstride, wd_gstride;
+    const int8_t* xq;
+    const uint16_t* xd;
+    const int32_t* col_off;  // [groups + 1] or null
+    const int32_t* col_idx;  // gather list or null
+    int32_t m;               // columns when col_off is null
+    int32_t groups;
+    float* y;
+    int64_t ldy;
+    const float* residual;
+    int64_t ldr;
+    int64_t ffn;             // EPI_SWIGLU: gate rows [0, ffn), up rows [ffn, 2 ffn)
+    int32_t max_cols;        // upper bound of columns per group (picks the tile)
+};
+
+int launch_gemv(const GemvArgs& a, int epi, hipStream_t s);
+
+// Q8_0 of [rows][k] fp32 (k % 32 == 0).
+int launch_quantize_q8(const float* x, int64_t rows, int64_t k, int8_t* xq, uint16_t* xd,
+                       hipStream_t s);
+
+// MFMA GEMM for many columns (prefill).  Same argument meaning as GemvArgs
+// without grouping (col_off must be null).
+int launch_gemm(const GemvArgs& a, int epi, hipStream_t s);
+
+// y = rmsnorm(x) rows; optional Q8_0 of y into (xq, xd); y may be null.
+int launch_rmsnorm_q8(const float* x, const float* gamma, int64_t rows, int64_t dim, float eps,
+                      float* y, int8_t* xq, uint16_t* xd, hipStream_t s);
+
+// Rotate q (heads_q) and k (heads_k) of every token in place, then store k
+// and v rows into the caches.  Token t's q head h starts at
+// base + t * tok_stride + q_off + h * hd, etc.
+int launch_rope_kv(float* base, int64_t tokens, int64_t tok_stride, int64_t q_off, int64_t nq,
+                   int64_t k_off, int64_t v_off, int64_t nkv, int64_t hd, const int32_t* pos,
+                   const int32_t* seq, float rope_base, uint16_t* k_cache, uint16_t* v_cache,
+                   int64_t cap, hipStream_t s);
+
+// Attention with explicit q/out token strides (elements).
+int launch_attention(const float* q, int64_t q_tok_stride, int64_t tokens, int64_t nq,
+                     int64_t nkv, int64_t hd, const uint16_t* kc, const uint16_t* vc, int64_t cap,
+                     const int32_t* pos, const int32_t* seq, float* out, int64_t out_tok_stride,
+                     void* ws, size_t ws_bytes, hipStream_t s);
+size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t hd, int64_t cap);
+
+}  // namespace qk

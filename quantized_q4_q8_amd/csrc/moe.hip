@@ -1,0 +1,289 @@
+// Routed mixture-of-experts layer with every expert resident in HBM.
+//
+// kerneldigest.dev, "Colibri: running 744B MoE models on consumer hardware
+// by streaming experts": a sigmoid router of the DeepSeek-V3 kind picks the
+// experts (System architecture; token flow step 2), the experts run int8
+// activation x int4 weight kernels (step 5) and their results are combined
+// into the token (step 6).  Each expert is a SwiGLU FFN (kenji.blog
+// TinyLLaMA-in-C++ guide, section 4.4).
+//
+// Pipeline (all on the caller's stream, deterministic, no float atomics):
+//  1. router logits r = x . W_r, H split into slices whose partial sums are
+//     added in a fixed order;
+//  2. per token: top-k on r (ties to the lower expert), sigmoid scores,
+//     weights normalized over the selection;
+//  3. stable counting sort of the (token, rank) pairs by expert -> per-expert
+//     column ranges, the token of every sorted column, and each pair's slot;
+//  4. Q8_0 of x; grouped gate/up GEMV with the SwiGLU epilogue over the
+//     sorted columns; Q8_0 of h; grouped down GEMV;
+//  5. per token, sum over ranks 0..k-1 of weight * expert output, in order.
+#include "internal.h"
+
+namespace qk {
+
+namespace {
+
+constexpr int RT = 4;        // tokens per router workgroup
+constexpr int RSLICE = 768;  // hidden elements per router slice
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct MoeWs {
+    float* rpart;       // [slices][T][E]
+    int32_t* off;       // [E + 1]
+    int32_t* col_tok;   // [P] token of each sorted column
+    int32_t* slot;      // [P] sorted column of pair p = t * k + rank
+    int8_t* xq;         // [T][H]
+    uint16_t* xd;       // [T][H/32]
+    float* h;           // [P][F]
+    int8_t* hq;         // [P][F]
+    uint16_t* hd;       // [P][F/32]
+    float* ys;          // [P][H]
+    size_t total;
+};
+
+MoeWs moe_layout(void* base, int64_t T, int64_t H, int64_t E, int64_t k, int64_t F) {
+    const int64_t P = T * k;
+    const int64_t slices = (H + RSLICE - 1) / RSLICE;
+    MoeWs w{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return base ? static_cast<char*>(base) + at : nullptr;
+    };
+    w.rpart = reinterpret_cast<float*>(take(sizeof(float) * slices * T * E));
+    w.off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+    w.col_tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
+    w.slot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
+    w.xq = reinterpret_cast<int8_t*>(take((size_t)(T * H)));
+    w.xd = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * T * (H / QBLK)));
+    w.h = reinterpret_cast<float*>(take(sizeof(float) * P * F));
+    w.hq = reinterpret_cast<int8_t*>(take((size_t)(P * F)));
+    w.hd = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * P * (F / QBLK)));
+    w.ys = reinterpret_cast<float*>(take(sizeof(float) * P * H));
+    w.total = o;
+    return w;
+}
+
+}  // namespace
+
+// rpart[s][t][e] = sum over h in slice s of x[t][h] * W_r[h][e]; thread = expert.
+__global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int64_t T, int64_t H,
+                                                const float* __restrict__ wr, int64_t E,
+                                                float* __restrict__ rpart) {
+    __shared__ float xs[RT][RSLICE];
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.y * RT;
+    const int64_t s = blockIdx.z;
+    const int64_t h0 = s * RSLICE;
+    const int64_t hn = min((int64_t)RSLICE, H - h0);
+    for (int64_t i = threadIdx.x; i < RT * RSLICE; i += 256) {
+        const int64_t tt = i / RSLICE, hh = i % RSLICE;
+        xs[tt][hh] = (t0 + tt < T && hh < hn) ? x[(t0 + tt) * H + h0 + hh] : 0.0f;
+    }
+    __syncthreads();
+    if (e >= E) return;
+    float acc[RT];
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0f;
+    for (int64_t hh = 0; hh < hn; ++hh) {
+        const float w = wr[(h0 + hh) * E + e];
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) acc[tt] = fmaf(xs[tt][hh], w, acc[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt)
+        if (t0 + tt < T) rpart[(s * T + t0 + tt) * E + e] = acc[tt];
+}
+
+// One workgroup (256 threads) per token: r[e] from the slices in order, then
+// top-k by repeated (value, lowest index) maxima over the experts not yet
+// taken (NaN never wins), then sigmoid weights normalized over the choice.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ rpart, int64_t slices,
+                                              int64_t T, int64_t E, int32_t k,
+                                              int32_t* __restrict__ sel_idx,
+                                              float* __restrict__ sel_w) {
+    __shared__ float rv[1024];
+    __shared__ unsigned char taken[1024];
+    __shared__ float wv[4];
+    __shared__ int wi[4];
+    __shared__ int chosen_e[32];
+    const int64_t t = blockIdx.x;
+    for (int64_t e = threadIdx.x; e < E; e += 256) {
+        float r = 0.0f;
+        for (int64_t s = 0; s < slices; ++s) r += rpart[(s * T + t) * E + e];
+        rv[e] = r;
+        taken[e] = 0;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < k; ++kk) {
+        float bv = -INFINITY;
+        int bi = INT32_MAX;
+        for (int64_t e = threadIdx.x; e < E; e += 256) {
+            if (taken[e]) continue;
+            const float v = rv[e];
+            if (v > bv || (v == bv && (int)e < bi)) { bv = v; bi = (int)e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, WAVE);
+            const int oi = __shfl_xor(bi, o, WAVE);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        }
+        if ((threadIdx.x & 63) == 0) { wv[threadIdx.x >> 6] = bv; wi[threadIdx.x >> 6] = bi; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < 4; ++w)
+                if (wv[w] > bv || (wv[w] == bv && wi[w] < bi)) { bv = wv[w]; bi = wi[w]; }
+            if (bi == INT32_MAX)  // only NaN left: the lowest index not taken
+                for (int e = 0; e < E; ++e)
+                    if (!taken[e]) { bi = e; break; }
+            chosen_e[kk] = bi;
+            taken[bi] = 1;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        float ssum = 0.0f;
+        float sv[32];
+        for (int kk = 0; kk < k; ++kk) {
+            sv[kk] = 1.0f / (1.0f + expf(-rv[chosen_e[kk]]));
+            ssum += sv[kk];
+        }
+        for (int kk = 0; kk < k; ++kk) {
+            sel_idx[t * k + kk] = chosen_e[kk];
+            sel_w[t * k + kk] = sv[kk] / ssum;
+        }
+    }
+}
+
+// Stable counting sort of the P = T * k pairs by expert (one workgroup of
+// 1024 threads).  Pairs are taken in chunks of 1024 in pair order; a pair's
+// column is off[e] + (pairs of e in earlier chunks) + (pairs of e earlier in
+// its chunk), so columns of an expert follow (token, rank) order.
+__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ sel_idx, int64_t P,
+                                                int32_t k, int64_t E, int32_t* __restrict__ off,
+                                                int32_t* __restrict__ col_tok,
+                                                int32_t* __restrict__ slot) {
+    __shared__ int cnt[1024];
+    __shared__ int base[1024];
+    __shared__ int chunk_e[1024];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    for (int64_t p = tid; p < P; p += 1024) atomicAdd(&cnt[sel_idx[p]], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = run;
+            base[e] = run;
+            run += cnt[e];
+        }
+        off[E] = run;
+    }
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < P; c0 += 1024) {
+        const int64_t p = c0 + tid;
+        const int e = p < P ? sel_idx[p] : -1;
+        chunk_e[tid] = e;
+        __syncthreads();
+        if (p < P) {
+            int rank = 0;
+            for (int q = 0; q < tid; ++q) rank += chunk_e[q] == e;
+            const int col = base[e] + rank;
+            col_tok[col] = (int32_t)(p / k);
+            slot[p] = col;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const int64_t n = min((int64_t)1024, P - c0);
+            for (int q = 0; q < n; ++q) base[chunk_e[q]] += 1;
+        }
+        __syncthreads();
+    }
+}
+
+// out[t][i] = sum_{r < k} sel_w[t][r] * ys[slot[t k + r]][i], ranks in order.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ys, int64_t H, int32_t k,
+                                                 const int32_t* __restrict__ slot,
+                                                 const float* __restrict__ sel_w,
+                                                 float* __restrict__ out) {
+    const int64_t t = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= H) return;
+    float acc = 0.0f;
+    for (int r = 0; r < k; ++r)
+        acc = fmaf(sel_w[t * k + r], ys[(int64_t)slot[t * k + r] * H + i], acc);
+    out[t * H + i] = acc;
+}
+
+}  // namespace qk
+
+using namespace qk;
+
+extern "C" size_t qk_moe_workspace(int64_t tokens, int64_t hidden, int64_t n_experts,
+                                   int32_t top_k, int64_t ffn) {
+    if (tokens < 0 || hidden <= 0 || n_experts <= 0 || top_k <= 0 || ffn <= 0) return 0;
+    return moe_layout(nullptr, tokens, hidden, n_experts, top_k, ffn).total;
+}
+
+extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden,
+                                   const float* w_router, int64_t n_experts, int32_t top_k,
+                                   const uint8_t* gate_up_q, const uint16_t* gate_up_d,
+                                   const uint8_t* down_q, const uint16_t* down_d, int64_t ffn,
+                                   float* y, int32_t* sel_idx, float* sel_w, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    QK_REQUIRE(tokens >= 0 && hidden > 0 && ffn > 0, QK_EINVAL);
+    QK_REQUIRE(n_experts > 0 && n_experts <= 1024 && top_k > 0 && top_k <= 32 &&
+                   top_k <= n_experts,
+               QK_EINVAL);
+    QK_REQUIRE(hidden % QBLK == 0 && ffn % QBLK == 0, QK_ESHAPE);
+    QK_REQUIRE(tokens * top_k <= INT32_MAX, QK_EINVAL);
+    if (tokens == 0) return QK_OK;
+    QK_REQUIRE(x && w_router && gate_up_q && gate_up_d && down_q && down_d && y && sel_idx && sel_w,
+               QK_EINVAL);
+    QK_REQUIRE(QK_ALIGNED(x, 16) && QK_ALIGNED(y, 16) && QK_ALIGNED(gate_up_q, 16) &&
+                   QK_ALIGNED(down_q, 16),
+               QK_EALIGN);
+    const MoeWs w = moe_layout(ws, tokens, hidden, n_experts, top_k, ffn);
+    QK_REQUIRE(ws && ws_bytes >= w.total, QK_EWORKSPACE);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t T = tokens, H = hidden, E = n_experts, F = ffn, P = T * top_k;
+    const int64_t slices = (H + RSLICE - 1) / RSLICE;
+
+    hipLaunchKernelGGL(k_router, dim3((unsigned)((E + 255) / 256), (unsigned)((T + RT - 1) / RT),
+                                      (unsigned)slices),
+                       dim3(256), 0, s, x, T, H, w_router, E, w.rpart);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(256), 0, s, w.rpart, slices, T, E, top_k,
+                       sel_idx, sel_w);
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, sel_idx, P, top_k, E, w.off, w.col_tok,
+                       w.slot);
+    int rc = launch_quantize_q8(x, T, H, w.xq, w.xd, s);
+    if (rc) return rc;
+
+    GemvArgs g{};
+    g.wq = gate_up_q; g.wd = gate_up_d; g.n = 2 * F; g.k = H;
+    g.wq_gstride = 2 * F * (H / 2); g.wd_gstride = 2 * F * (H / QBLK);
+    g.xq = w.xq; g.xd = w.xd; g.col_off = w.off; g.col_idx = w.col_tok;
+    g.m = 0; g.groups = (int32_t)E; g.y = w.h; g.ldy = F; g.residual = nullptr; g.ldr = 0;
+    g.ffn = F; g.max_cols = 4;
+    rc = launch_gemv(g, EPI_SWIGLU, s);
+    if (rc) return rc;
+    rc = launch_quantize_q8(w.h, P, F, w.hq, w.hd, s);
+    if (rc) return rc;
+
+    GemvArgs d{};
+    d.wq = down_q; d.wd = down_d; d.n = H; d.k = F;
+    d.wq_gstride = H * (F / 2); d.wd_gstride = H * (F / QBLK);
+    d.xq = w.hq; d.xd = w.hd; d.col_off = w.off; d.col_idx = nullptr;
+    d.m = 0; d.groups = (int32_t)E; d.y = w.ys; d.ldy = H; d.residual = nullptr; d.ldr = 0;
+    d.ffn = 0; d.max_cols = 4;
+    rc = launch_gemv(d, EPI_STORE, s);
+    if (rc) return rc;
+
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, s,
+                       w.ys, H, top_k, w.slot, sel_w, y);
+    return qk_launch_status();
+}

@@ -1,0 +1,116 @@
+"""A LLaMA-shaped decoder built from the libqk entry points.
+
+Composition only: embedding lookup, ``layer_forward`` per layer, final
+RMSNorm, Q8_0, the LM-head quantized matmul and greedy argmax, all enqueued on
+the current stream [kenji.blog TinyLLaMA-in-C++ guide, section 2: embedding,
+transformer blocks, RMSNorm, LM head, logits, next token].  Weights arrive as
+fp32 host arrays and are quantized to Q4_0 on the device by the library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import (LayerWeights, Workspace, layer_cfg, layer_forward, qk_argmax, qk_embed_lookup,
+               qk_layer_workspace, qk_quantize_q4_0, qmatmul_q4_0_q8_0, quantize_q8_0, rmsnorm)
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Host array -> device tensor (uint16 fp16 bit patterns travel as int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def quantize_on_device(w32: np.ndarray | torch.Tensor, device="cuda"):
+    """fp32 [n][k] (host or device) -> Q4_0 (nibbles, scales) on the device."""
+    t = w32 if isinstance(w32, torch.Tensor) else to_device(w32, device)
+    q, d = qk_quantize_q4_0(t)
+    return q, d
+
+
+def layer_to_device(wf: dict, device="cuda") -> LayerWeights:
+    """fp32 layer dict (w_qkv, w_o, w_gate_up, w_down, gamma_attn, gamma_ffn) -> device Q4_0."""
+    qkv = quantize_on_device(wf["w_qkv"], device)
+    o = quantize_on_device(wf["w_o"], device)
+    gu = quantize_on_device(wf["w_gate_up"], device)
+    dn = quantize_on_device(wf["w_down"], device)
+    return LayerWeights(qkv[0], qkv[1], o[0], o[1], gu[0], gu[1], dn[0], dn[1],
+                        to_device(wf["gamma_attn"], device), to_device(wf["gamma_ffn"], device))
+
+
+@dataclass
+class DecoderShape:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int            # padded to a multiple of 32
+    eps: float
+    rope_base: float
+    layers: int
+    vocab: int
+    cap: int
+    seqs: int = 1
+
+
+class Decoder:
+    """Layers, embedding, final norm and LM head resident on one device, plus
+    fp16 KV caches [layer][seqs][n_kv][cap][hd]."""
+
+    def __init__(self, shape: DecoderShape, layers: list[LayerWeights], embed: torch.Tensor,
+                 gamma_final: torch.Tensor, lm_q: torch.Tensor, lm_d: torch.Tensor, device="cuda"):
+        self.s = shape
+        self.layers = layers
+        self.structs = [lw.struct() for lw in layers]
+        self.embed = embed
+        self.gamma_final = gamma_final
+        self.lm_q, self.lm_d = lm_q, lm_d
+        self.cfg = layer_cfg(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                             shape.ffn, shape.eps, shape.rope_base, shape.cap)
+        kv_shape = (shape.layers, shape.seqs, shape.n_kv_heads, shape.cap, shape.head_dim)
+        self.k_cache = torch.zeros(kv_shape, dtype=torch.int16, device=device)
+        self.v_cache = torch.zeros(kv_shape, dtype=torch.int16, device=device)
+        self.ws = Workspace()
+        self.device = device
+
+    def reserve(self, tokens: int) -> None:
+        """Size the workspace for calls of up to `tokens` tokens (before graph capture)."""
+        self.ws.reserve(qk_layer_workspace(self.cfg, tokens), self.device)
+
+    def hidden_states(self, ids: torch.Tensor, pos: torch.Tensor, seq: torch.Tensor,
+                      x: torch.Tensor | None = None) -> torch.Tensor:
+        """Embedding and every layer for the tokens ids [T] at (pos, seq)."""
+        x = qk_embed_lookup(self.embed, ids, out=x)
+        for li, st in enumerate(self.structs):
+            layer_forward(st, self.cfg, x, pos, seq, self.k_cache[li], self.v_cache[li], ws=self.ws)
+        return x
+
+    def logits(self, x: torch.Tensor, out: torch.Tensor | None = None,
+               scratch: dict | None = None) -> torch.Tensor:
+        sc = scratch if scratch is not None else {}
+        xn = rmsnorm(x, self.gamma_final, self.s.eps, out=sc.get("xn"))
+        xq, xd = quantize_q8_0(xn, out_q=sc.get("xq"), out_d=sc.get("xd"))
+        return qmatmul_q4_0_q8_0(self.lm_q, self.lm_d, xq, xd, out=out)
+
+    def step(self, ids: torch.Tensor, pos: torch.Tensor, seq: torch.Tensor,
+             bufs: dict | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+        """One forward over ids [T]: returns (logits [T][V], argmax ids [T])."""
+        b = bufs if bufs is not None else {}
+        x = self.hidden_states(ids, pos, seq, x=b.get("x"))
+        lg = self.logits(x, out=b.get("logits"), scratch=b)
+        nxt = qk_argmax(lg, out=b.get("next"))
+        return lg, nxt
+
+    def step_buffers(self, tokens: int) -> dict:
+        """Preallocated buffers so that `step` allocates nothing (graph capture)."""
+        dev, H, V = self.device, self.s.hidden, self.s.vocab
+        return dict(x=torch.empty((tokens, H), dtype=torch.float32, device=dev),
+                    xn=torch.empty((tokens, H), dtype=torch.float32, device=dev),
+                    xq=torch.empty((tokens, H), dtype=torch.int8, device=dev),
+                    xd=torch.empty((tokens, H // 32), dtype=torch.int16, device=dev),
+                    logits=torch.empty((tokens, V), dtype=torch.float32, device=dev),
+                    next=torch.empty((tokens,), dtype=torch.int32, device=dev))

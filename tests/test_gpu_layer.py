@@ -1,0 +1,173 @@
+"""GPU parity of layer_forward and moe_route_and_apply against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from quantized_q4_q8_amd.model import layer_to_device
+from synth import workloads as W
+from tests.util import LAYER_TOL, dev, host, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_layer(wf):
+    wl = {}
+    for name, key in [("w_qkv", "w_qkv"), ("w_o", "w_o"), ("w_gate_up", "w_gu"), ("w_down", "w_down")]:
+        wl[key + "_q"], wl[key + "_d"] = oracle.quantize_q4_0(wf[name])
+    wl["gamma_attn"], wl["gamma_ffn"] = wf["gamma_attn"], wf["gamma_ffn"]
+    return wl
+
+
+def check_weights_identical(lw, wl):
+    """The device quantizer produced the very bytes the oracle uses."""
+    pairs = [(lw.w_qkv_q, wl["w_qkv_q"]), (lw.w_qkv_d, wl["w_qkv_d"]), (lw.w_o_q, wl["w_o_q"]),
+             (lw.w_gate_up_q, wl["w_gu_q"]), (lw.w_down_d, wl["w_down_d"])]
+    for t, a in pairs:
+        assert np.array_equal(host(t, a.dtype), a)
+
+
+def test_layer_small_prefill_then_self_fed_decode(gpu_lib):
+    """The one-layer workload: 16-token prefill (MFMA GEMM path), then 16 decode
+    steps (GEMV path) where each side feeds back its own last output."""
+    qk = gpu_lib
+    spec = W.LAYER_SMALL
+    g, seed, cap = spec["geometry"], spec["seed"], spec["cap"]
+    say(f"layer_forward small: H={g.hidden} nq={g.n_q_heads} nkv={g.n_kv_heads} F={g.ffn}")
+    wf = W.layer_weights_f32(seed, 0, g)
+    wl = oracle_layer(wf)
+    lw = layer_to_device(wf)
+    check_weights_identical(lw, wl)
+    cfg = qk.layer_cfg(**g.cfg(cap))
+    P = spec["prompt"]
+    x = synth.normal(seed, W.TID_X, (P, g.hidden))
+    kshape = (1, g.n_kv_heads, cap, g.head_dim)
+    kc, vc = np.zeros(kshape, np.uint16), np.zeros(kshape, np.uint16)
+    kcg, vcg = dev(kc), dev(vc)
+    pos = np.arange(P, dtype=np.int32)
+    seq = np.zeros(P, np.int32)
+    ref = oracle.layer_forward(wl, g.cfg(cap), x, pos, seq, kc, vc)
+    xg = dev(x)
+    qk.layer_forward(lw, cfg, xg, dev(pos), dev(seq), kcg, vcg)
+    assert rel_err(host(xg), ref) < LAYER_TOL
+    kf = oracle.f16_to_f32(kc)
+    assert rel_err(oracle.f16_to_f32(host(kcg, np.uint16)), kf) < LAYER_TOL
+    o_in, g_in = ref[-1:], host(xg)[-1:]
+    for step in range(spec["decode"]):
+        p = np.array([P + step], np.int32)
+        s0 = np.zeros(1, np.int32)
+        o_out = oracle.layer_forward(wl, g.cfg(cap), o_in, p, s0, kc, vc)
+        xs = dev(g_in)
+        qk.layer_forward(lw, cfg, xs, dev(p), dev(s0), kcg, vcg)
+        g_out = host(xs)
+        assert rel_err(g_out, o_out) < LAYER_TOL, f"decode step {step}"
+        o_in, g_in = o_out, g_out
+
+
+@pytest.mark.parametrize("tokens", [5, 40])
+def test_layer_ragged_sequences(gpu_lib, tokens):
+    """Tokens of three sequences at scattered positions, with prefilled caches;
+    5 tokens run the GEMV path, 40 the MFMA path."""
+    qk = gpu_lib
+    g = W.Geometry(512, 16, 4, 32, 352)
+    cap = 96
+    say(f"layer_forward ragged tokens={tokens}")
+    wf = W.layer_weights_f32(40, 1, g)
+    wl = oracle_layer(wf)
+    lw = layer_to_device(wf)
+    kc, vc = W.kv_prefill_f16(40, 1, g.n_kv_heads, cap, g.head_dim, 50, seqs=3)
+    kc, vc = kc.view(np.uint16).copy(), vc.view(np.uint16).copy()
+    kcg, vcg = dev(kc), dev(vc)
+    seq = (np.arange(tokens) % 3).astype(np.int32)
+    pos = (50 + np.arange(tokens) // 3).astype(np.int32)
+    x = synth.normal(40, 5, (tokens, g.hidden))
+    ref = oracle.layer_forward(wl, g.cfg(cap), x, pos, seq, kc, vc)
+    xg = dev(x)
+    qk.layer_forward(lw, qk.layer_cfg(**g.cfg(cap)), xg, dev(pos), dev(seq), kcg, vcg)
+    assert rel_err(host(xg), ref) < LAYER_TOL
+
+
+def test_layer_decode_equals_prefill_last_row(gpu_lib):
+    qk = gpu_lib
+    g = W.LAYER_SMALL["geometry"]
+    cap = 32
+    say("layer_forward decode == prefill last row (GPU)")
+    lw = layer_to_device(W.layer_weights_f32(41, 0, g))
+    cfg = qk.layer_cfg(**g.cfg(cap))
+    x = synth.normal(41, 1, (12, g.hidden))
+    shape = (1, g.n_kv_heads, cap, g.head_dim)
+    pos = np.arange(12, dtype=np.int32)
+    seq = np.zeros(12, np.int32)
+    ka, va = torch.zeros(shape, dtype=torch.int16, device="cuda"), torch.zeros(shape, dtype=torch.int16, device="cuda")
+    full = dev(x)
+    qk.layer_forward(lw, cfg, full, dev(pos), dev(seq), ka, va)
+    kb, vb = torch.zeros_like(ka), torch.zeros_like(va)
+    part = dev(x[:11])
+    qk.layer_forward(lw, cfg, part, dev(pos[:11]), dev(seq[:11]), kb, vb)
+    last = dev(x[11:])
+    qk.layer_forward(lw, cfg, last, dev(pos[11:]), dev(seq[11:]), kb, vb)
+    assert rel_err(host(last), host(full)[11:]) < LAYER_TOL
+
+
+# ---------------------------------------------------------------- MoE
+def experts_f32(seed, E, H, F):
+    gus, dns = [], []
+    for e in range(E):
+        gu, dn = W.expert_weights_f32(seed, e, H, F)
+        gus.append(gu)
+        dns.append(dn)
+    return np.stack(gus), np.stack(dns)
+
+
+def check_routing(sel_g, w_g, sel_o, w_o, logits):
+    """Selections must agree except where the oracle's k-th and (k+1)-th
+    logits are within 1e-5 (either choice is correct there)."""
+    k = sel_o.shape[1]
+    for t in range(sel_o.shape[0]):
+        if np.array_equal(sel_g[t], sel_o[t]):
+            assert np.allclose(w_g[t], w_o[t], rtol=1e-5, atol=1e-7)
+            continue
+        srt = np.sort(logits[t])[::-1]
+        assert srt[k - 1] - srt[k] < 1e-5, f"token {t}: selection differs without a near tie"
+
+
+@pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (1, 128, 8, 32, 1)])
+def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
+    qk = gpu_lib
+    say(f"moe_route_and_apply T={T} H={H} E={E} F={F} k={k}")
+    seed = 50 + T
+    x = synth.normal(seed, W.TID_X, (T, H))
+    wr = synth.normal(seed, W.TID_ROUTER, (H, E), 0.02)
+    gu, dn = experts_f32(seed, E, H, F)
+    guq = np.stack([oracle.quantize_q4_0(a)[0] for a in gu])
+    gud = np.stack([oracle.quantize_q4_0(a)[1] for a in gu])
+    dnq = np.stack([oracle.quantize_q4_0(a)[0] for a in dn])
+    dnd = np.stack([oracle.quantize_q4_0(a)[1] for a in dn])
+    out, sel, w = oracle.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd)
+    _, _, logits = oracle.moe_route(x, wr, k, return_logits=True)
+    y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
+    sel_g, w_g = host(sg), host(wg)
+    check_routing(sel_g, w_g, sel, w, logits)
+    if np.array_equal(sel_g, sel):
+        assert rel_err(host(y), out) < LAYER_TOL
+    # every selection is a set of distinct experts and weights sum to 1
+    assert all(len(set(r)) == k for r in sel_g)
+    assert np.allclose(w_g.sum(1), 1.0, atol=1e-6)
+
+
+def test_moe_zero_router_ties(gpu_lib):
+    qk = gpu_lib
+    T, H, E, F, k = 4, 64, 12, 32, 5
+    say("moe zero router")
+    x = synth.normal(60, 1, (T, H))
+    gu, dn = experts_f32(60, E, H, F)
+    guq = np.stack([oracle.quantize_q4_0(a)[0] for a in gu])
+    gud = np.stack([oracle.quantize_q4_0(a)[1] for a in gu])
+    dnq = np.stack([oracle.quantize_q4_0(a)[0] for a in dn])
+    dnd = np.stack([oracle.quantize_q4_0(a)[1] for a in dn])
+    wr = np.zeros((H, E), np.float32)
+    out, sel, w = oracle.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd)
+    y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
+    assert np.all(host(sg) == np.arange(k)) and np.all(host(wg) == np.float32(1 / k))
+    assert rel_err(host(y), out) < LAYER_TOL

@@ -1,0 +1,248 @@
+"""GPU parity of each libqk entry point against the CPU oracle, through the
+C-ABI binding.  Integer and byte outputs are compared bit for bit; fp32
+outputs with the relative error of tests/util.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads as W
+from tests.util import LAYER_TOL, dev, host, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- quantizers
+Q8_SHAPES = [(1, 32), (3, 2048), (5, 5632), (64, 6144), (17, 704), (2, 256)]
+
+
+@pytest.mark.parametrize("rows,k", Q8_SHAPES)
+def test_quantize_q8_0_bit_exact(gpu_lib, rows, k):
+    qk = gpu_lib
+    say(f"quantize_q8_0 rows={rows} k={k}")
+    x = synth.normal(100, rows * 7 + k, (rows, k))
+    q, d = qk.quantize_q8_0(dev(x))
+    oq, od = oracle.quantize_q8_0(x)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(d, np.uint16), od)
+
+
+def test_quantize_q8_0_edge_values(gpu_lib):
+    qk = gpu_lib
+    say("quantize_q8_0 edge values")
+    blocks = []
+    b = np.zeros(32, np.float32); blocks.append(b)                       # all zero
+    b = np.zeros(32, np.float32); b[0] = 127; b[1:9] = [2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5, -0.0]
+    blocks.append(b)                                                      # ties
+    blocks.append(np.full(32, 1e-40, np.float32))                         # subnormal inputs
+    b = synth.normal(101, 1, 32) * np.float32(1e-6); blocks.append(b)     # fp16-subnormal scale
+    b = synth.normal(101, 2, 32) * np.float32(1e-9); blocks.append(b)     # scale underflows fp16
+    b = synth.normal(101, 3, 32) * np.float32(1e7); blocks.append(b)      # scale overflows fp16
+    b = np.arange(32, dtype=np.float32) - 15.5; blocks.append(b)
+    b = np.zeros(32, np.float32); b[31] = -3.0; blocks.append(b)
+    # every x/d that lands exactly on a .5 boundary at d = 1
+    b = np.concatenate([[127.0], np.arange(31, dtype=np.float32) * 2 + 0.5]).astype(np.float32)
+    blocks.append(b)
+    x = np.stack(blocks).reshape(1, -1).astype(np.float32)
+    q, d = qk.quantize_q8_0(dev(x))
+    oq, od = oracle.quantize_q8_0(x)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(d, np.uint16), od)
+
+
+@pytest.mark.parametrize("n,k", [(7, 64), (384, 256), (2560, 2048), (33, 5632)])
+def test_quantize_q4_0_bit_exact(gpu_lib, n, k):
+    qk = gpu_lib
+    say(f"qk_quantize_q4_0 n={n} k={k}")
+    w = synth.normal(102, n + k, (n, k), 0.02)
+    w[0, :32] = 0.0
+    if n > 1:
+        w[1, :32] = np.arange(32, dtype=np.float32) * np.float32(0.5) - 7.0  # ties at delta = 1
+    q, d = qk.qk_quantize_q4_0(dev(w))
+    oq, od = oracle.quantize_q4_0(w)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(d, np.uint16), od)
+
+
+@pytest.mark.parametrize("n,k,m", [(5, 32, 1), (64, 2048, 3), (37, 704, 2)])
+def test_block_dots_bit_exact_on_any_bytes(gpu_lib, n, k, m):
+    qk = gpu_lib
+    say(f"qk_block_dots n={n} k={k} m={m}")
+    r = np.random.default_rng(n * k + m)
+    wq = r.integers(0, 256, (n, k // 2), dtype=np.uint8)     # every nibble, including code -8
+    xq = r.integers(-128, 128, (m, k), dtype=np.int8)
+    wq[0] = 0x00
+    xq[0, :32] = -127
+    isum = qk.qk_block_dots_q4_0_q8_0(dev(wq), dev(xq))
+    assert np.array_equal(host(isum), oracle.block_dots(wq, k, xq))
+
+
+# ---------------------------------------------------------------- matmul
+MM_CASES = [(5632, 2048, 1), (2048, 5632, 1), (5632, 2048, 8), (2048, 5632, 8),
+            (384, 256, 16), (37, 704, 3), (100, 32, 2), (256, 2048, 9), (130, 2048, 33),
+            (300, 6144, 130), (64, 256, 1), (4096, 6144, 2)]
+
+
+@pytest.mark.parametrize("n,k,m", MM_CASES)
+def test_qmatmul_matches_oracle(gpu_lib, n, k, m):
+    qk = gpu_lib
+    say(f"qmatmul n={n} k={k} m={m}")
+    w = synth.normal(103, n + 3 * k, (n, k), 0.02)
+    x = synth.normal(104, n + 5 * k + m, (m, k))
+    wq, wd = oracle.quantize_q4_0(w)
+    xq, xd = oracle.quantize_q8_0(x)
+    y = qk.qmatmul_q4_0_q8_0(dev(wq), dev(wd), dev(xq), dev(xd))
+    ref = oracle.qmatmul(wq, wd, xq, xd)
+    assert rel_err(host(y), ref) < 1e-5
+
+
+def test_qmatmul_zero_and_empty(gpu_lib):
+    qk = gpu_lib
+    say("qmatmul zero weights, m = 0")
+    wq = np.full((40, 64), 0x88, np.uint8)
+    wd = np.zeros((40, 4), np.uint16)
+    x = synth.normal(105, 0, (3, 128))
+    xq, xd = oracle.quantize_q8_0(x)
+    y = qk.qmatmul_q4_0_q8_0(dev(wq), dev(wd), dev(xq), dev(xd))
+    assert np.all(host(y) == 0)
+    empty = torch.empty((0, 128), dtype=torch.int8, device="cuda")
+    emptyd = torch.empty((0, 4), dtype=torch.int16, device="cuda")
+    assert qk.qmatmul_q4_0_q8_0(dev(wq), dev(wd), empty, emptyd).shape == (0, 40)
+
+
+# ---------------------------------------------------------------- element-wise
+@pytest.mark.parametrize("rows,dim", [(16, 256), (3, 2048), (1, 6144), (5, 8)])
+def test_rmsnorm(gpu_lib, rows, dim):
+    qk = gpu_lib
+    say(f"rmsnorm rows={rows} dim={dim}")
+    x = synth.normal(106, dim, (rows, dim))
+    g = synth.normal(106, 1, dim, 0.02, mean=1.0)
+    y = qk.rmsnorm(dev(x), dev(g), 1e-5)
+    assert rel_err(host(y), oracle.rmsnorm(x, g, 1e-5)) < 2e-6
+
+
+@pytest.mark.parametrize("tokens,heads,hd", [(16, 12, 32), (3, 36, 64), (1, 1, 2)])
+def test_rope(gpu_lib, tokens, heads, hd):
+    qk = gpu_lib
+    say(f"rope tokens={tokens} heads={heads} hd={hd}")
+    x = synth.normal(107, heads, (tokens, heads, hd))
+    pos = np.concatenate([[0], synth.randint(107, 2, tokens - 1, 2176)]).astype(np.int32)
+    xg = dev(x)
+    qk.rope(xg, dev(pos), 10000.0)
+    ref = oracle.rope(x, pos, 10000.0)
+    got = host(xg)
+    assert np.array_equal(got[0], x[0])       # position 0 is the identity
+    assert rel_err(got, ref) < 2e-6
+
+
+def test_swiglu(gpu_lib):
+    qk = gpu_lib
+    say("swiglu")
+    g = synth.normal(108, 0, 5000) * np.float32(6)
+    u = synth.normal(108, 1, 5000)
+    h = qk.swiglu(dev(g), dev(u))
+    assert rel_err(host(h), oracle.swiglu(g, u)) < 2e-6
+
+
+def test_kv_append_bit_exact(gpu_lib):
+    qk = gpu_lib
+    say("qk_kv_append")
+    nkv, cap, hd = 4, 40, 64
+    k = synth.normal(109, 0, (6, nkv, hd))
+    v = synth.normal(109, 1, (6, nkv, hd))
+    pos = np.array([0, 39, 5, 5, 17, 2], np.int32)
+    seq = np.array([0, 0, 1, 2, 2, 1], np.int32)
+    kc = np.zeros((3, nkv, cap, hd), np.uint16)
+    vc = np.zeros_like(kc)
+    kcg, vcg = dev(kc), dev(vc)
+    qk.qk_kv_append(dev(k), dev(v), dev(pos), dev(seq), kcg, vcg)
+    oracle.kv_append(k, v, pos, seq, kc, vc)
+    assert np.array_equal(host(kcg, np.uint16), kc)
+    assert np.array_equal(host(vcg, np.uint16), vc)
+
+
+def test_embed_and_argmax(gpu_lib):
+    qk = gpu_lib
+    say("qk_embed_lookup, qk_argmax")
+    table = synth.normal(110, 0, (1000, 64))
+    ids = synth.randint(110, 1, 9, 1000)
+    x = qk.qk_embed_lookup(dev(table), dev(ids))
+    assert np.array_equal(host(x), oracle.embed_lookup(table, ids))
+    logits = synth.normal(110, 2, (5, 32000))
+    logits[1, 77] = logits[1, 9000] = 50.0          # tie -> lowest index
+    logits[2, :] = -3.0                              # all equal -> 0
+    logits[3, 31999] = 60.0                          # last element
+    idx = qk.qk_argmax(dev(logits))
+    assert host(idx).tolist() == oracle.argmax(logits).tolist()
+    assert host(idx)[1] == 77 and host(idx)[2] == 0 and host(idx)[3] == 31999
+
+
+# ---------------------------------------------------------------- attention
+def _cache(seed, seqs, nkv, cap, hd, filled):
+    kc = np.zeros((seqs, nkv, cap, hd), np.uint16)
+    vc = np.zeros_like(kc)
+    kc[:, :, :filled] = synth.normal(seed, 1, (seqs, nkv, filled, hd)).astype(np.float16).view(np.uint16)
+    vc[:, :, :filled] = synth.normal(seed, 2, (seqs, nkv, filled, hd)).astype(np.float16).view(np.uint16)
+    return kc, vc
+
+
+ATT_CASES = [
+    # (tokens, nq, nkv, hd, cap, seqs, pos recipe)
+    (16, 8, 2, 32, 32, 1, "prefill"),
+    (1, 32, 4, 64, 2176, 1, "decode2048"),
+    (6, 32, 4, 64, 2176, 3, "ragged"),
+    (3, 8, 8, 64, 130, 1, "mha"),
+    (2, 16, 1, 32, 70, 2, "mqa"),
+    (1, 32, 4, 64, 2176, 1, "first"),
+]
+
+
+@pytest.mark.parametrize("tokens,nq,nkv,hd,cap,seqs,recipe", ATT_CASES)
+def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
+    qk = gpu_lib
+    say(f"gqa_attention {recipe} tokens={tokens} nq={nq} nkv={nkv} hd={hd} cap={cap}")
+    kc, vc = _cache(111, seqs, nkv, cap, hd, cap)
+    q = synth.normal(111, 3, (tokens, nq, hd))
+    if recipe == "prefill":
+        pos = np.arange(tokens, dtype=np.int32)
+    elif recipe == "decode2048":
+        pos = np.array([2048], np.int32)
+    elif recipe == "first":
+        pos = np.array([0], np.int32)
+    elif recipe == "ragged":
+        pos = np.array([2175, 0, 63, 64, 1000, 129], np.int32)
+    else:
+        pos = (synth.randint(111, 4, tokens, cap)).astype(np.int32)
+    seq = (np.arange(tokens) % seqs).astype(np.int32)
+    out = qk.gqa_attention(dev(q), dev(kc), dev(vc), dev(pos), dev(seq))
+    ref = oracle.gqa_attention(q, kc, vc, pos, seq)
+    assert rel_err(host(out), ref) < 1e-5
+
+
+# ---------------------------------------------------------------- errors
+def test_error_codes_and_nothing_enqueued(gpu_lib):
+    qk = gpu_lib
+    say("error paths")
+    L = qk.load()
+    x = torch.full((2, 40), 7.0, dtype=torch.float32, device="cuda")
+    q = torch.full((2, 40), 5, dtype=torch.int8, device="cuda")
+    d = torch.full((2, 2), 3, dtype=torch.int16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.quantize_q8_0(x.data_ptr(), 2, 40, q.data_ptr(), d.data_ptr(), s) == qk.QK_ESHAPE
+    assert L.quantize_q8_0(x.data_ptr() + 4, 1, 32, q.data_ptr(), d.data_ptr(), s) == qk.QK_EALIGN
+    assert L.quantize_q8_0(None, 1, 32, q.data_ptr(), d.data_ptr(), s) == qk.QK_EINVAL
+    qa = torch.zeros((4, 2, 32), dtype=torch.float32, device="cuda")
+    kc = torch.zeros((1, 1, 8, 32), dtype=torch.int16, device="cuda")
+    pos = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = torch.full((4, 2, 32), 9.0, dtype=torch.float32, device="cuda")
+    rc = L.gqa_attention(qa.data_ptr(), 4, 2, 1, 32, kc.data_ptr(), kc.data_ptr(), 8,
+                         pos.data_ptr(), pos.data_ptr(), out.data_ptr(), ws.data_ptr(), 16, s)
+    assert rc == qk.QK_EWORKSPACE
+    rc = L.gqa_attention(qa.data_ptr(), 4, 3, 2, 32, kc.data_ptr(), kc.data_ptr(), 8,
+                         pos.data_ptr(), pos.data_ptr(), out.data_ptr(), ws.data_ptr(), 16, s)
+    assert rc == qk.QK_ESHAPE
+    torch.cuda.synchronize()
+    # nothing was enqueued: outputs untouched
+    assert torch.all(q == 5) and torch.all(d == 3) and torch.all(out == 9.0)
