@@ -105,6 +105,14 @@ int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_t n, int64_
                       const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y,
                       void* stream);
 
+/* Gate/up projection fused with SwiGLU [GUIDE 4.4: SwiGLU(x) = swish(x W_gate)
+ * * (x W_up), built from silu and mul on the two matmul outputs]: W [2 ffn][k]
+ * Q4_0 holds the ffn gate rows, then the ffn up rows; for every token t and
+ * f < ffn, h[t][f] = swish(g) * u with g, u the quantized matmul outputs of
+ * rows f and ffn + f (as in qmatmul_q4_0_q8_0).  h [m][ffn] fp32. */
+int qk_gate_up_swiglu(const uint8_t* w_q, const uint16_t* w_d, int64_t ffn, int64_t k,
+                      const int8_t* x_q, const uint16_t* x_d, int64_t m, float* h, void* stream);
+
 /* The per-block int32 dot products themselves, for bit-exact checking:
  * isum[t][r][b] for t < m, r < n, b < k/32 (int32 [m][n][k/32]). */
 int qk_block_dots_q4_0_q8_0(const uint8_t* w_q, int64_t n, int64_t k, const int8_t* x_q,

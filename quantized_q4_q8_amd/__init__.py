@@ -52,6 +52,7 @@ _SIGS = {
     "qk_q4_0_from_blocks": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "qmatmul_q4_0_q8_0": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _P], ctypes.c_int),
     "qk_block_dots_q4_0_q8_0": ([_P, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "qk_gate_up_swiglu": ([_P, _P, _I64, _I64, _P, _P, _I64, _P, _P], ctypes.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F32, _P, _P], ctypes.c_int),
     "rope": ([_P, _I64, _I64, _I64, _P, _F32, _P], ctypes.c_int),
     "swiglu": ([_P, _P, _I64, _P, _P], ctypes.c_int),
@@ -188,6 +189,17 @@ def qmatmul_q4_0_q8_0(w_q, w_d, x_q, x_d, out=None):
                                     k, _dev(x_q, torch.int8, "x_q"), _dev16(x_d, "x_d"), m,
                                     _dev(y, torch.float32, "y"), _stream()), "qmatmul_q4_0_q8_0")
     return y
+
+
+def qk_gate_up_swiglu(w_q, w_d, x_q, x_d, out=None):
+    """h [m][ffn] = swish(W_gate x) * (W_up x), W = [gate rows; up rows] Q4_0 [2 ffn][k]."""
+    ffn, k = w_q.shape[0] // 2, w_q.shape[1] * 2
+    m = x_q.numel() // k
+    h = _out(out, (m, ffn), torch.float32, x_q)
+    _check(load().qk_gate_up_swiglu(_dev(w_q, torch.uint8, "w_q"), _dev16(w_d, "w_d"), ffn, k,
+                                    _dev(x_q, torch.int8, "x_q"), _dev16(x_d, "x_d"), m,
+                                    _dev(h, torch.float32, "h"), _stream()), "qk_gate_up_swiglu")
+    return h
 
 
 def qk_block_dots_q4_0_q8_0(w_q, x_q, out=None):

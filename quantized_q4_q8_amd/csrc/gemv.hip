@@ -239,3 +239,23 @@ extern "C" int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_
     if (m > 8) return launch_gemm(a, EPI_STORE, (hipStream_t)stream);
     return launch_gemv(a, EPI_STORE, (hipStream_t)stream);
 }
+
+extern "C" int qk_gate_up_swiglu(const uint8_t* w_q, const uint16_t* w_d, int64_t ffn, int64_t k,
+                                 const int8_t* x_q, const uint16_t* x_d, int64_t m, float* h,
+                                 void* stream) {
+    QK_REQUIRE(ffn >= 0 && m >= 0 && k > 0, QK_EINVAL);
+    QK_REQUIRE(k % QBLK == 0, QK_ESHAPE);
+    QK_REQUIRE(m <= INT32_MAX && ffn <= INT32_MAX / 4, QK_EINVAL);
+    if (ffn == 0 || m == 0) return QK_OK;
+    QK_REQUIRE(w_q && w_d && x_q && x_d && h, QK_EINVAL);
+    QK_REQUIRE(QK_ALIGNED(w_q, 16) && QK_ALIGNED(x_q, 16) && QK_ALIGNED(w_d, 2) &&
+                   QK_ALIGNED(x_d, 2) && QK_ALIGNED(h, 4),
+               QK_EALIGN);
+    GemvArgs a{};
+    a.wq = w_q; a.wd = w_d; a.n = 2 * ffn; a.k = k;
+    a.xq = x_q; a.xd = x_d; a.m = (int32_t)m; a.groups = 1;
+    a.y = h; a.ldy = ffn; a.residual = nullptr; a.ldr = 0; a.ffn = ffn;
+    a.max_cols = (int32_t)m;
+    if (m > 8) return launch_gemm(a, EPI_SWIGLU, (hipStream_t)stream);
+    return launch_gemv(a, EPI_SWIGLU, (hipStream_t)stream);
+}

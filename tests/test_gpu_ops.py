@@ -97,6 +97,20 @@ def test_qmatmul_matches_oracle(gpu_lib, n, k, m):
     assert rel_err(host(y), ref) < 1e-5
 
 
+@pytest.mark.parametrize("ffn,k,m", [(5632, 2048, 1), (704, 256, 16), (96, 64, 5), (2048, 6144, 3)])
+def test_gate_up_swiglu(gpu_lib, ffn, k, m):
+    qk = gpu_lib
+    say(f"qk_gate_up_swiglu ffn={ffn} k={k} m={m}")
+    w = synth.normal(112, ffn + k, (2 * ffn, k), 0.02)
+    x = synth.normal(113, ffn + k + m, (m, k))
+    wq, wd = oracle.quantize_q4_0(w)
+    xq, xd = oracle.quantize_q8_0(x)
+    h = qk.qk_gate_up_swiglu(dev(wq), dev(wd), dev(xq), dev(xd))
+    gu = oracle.qmatmul(wq, wd, xq, xd)
+    ref = oracle.swiglu(gu[:, :ffn], gu[:, ffn:])
+    assert rel_err(host(h), ref) < 1e-5
+
+
 def test_qmatmul_zero_and_empty(gpu_lib):
     qk = gpu_lib
     say("qmatmul zero weights, m = 0")
