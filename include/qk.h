@@ -212,13 +212,24 @@ typedef struct qk_layer_cfg {
  *   x2 = x1 + w_down . Q8_0(swiglu(g, up))
  * x [tokens][hidden] fp32 is updated in place to x2.  Tokens may belong to
  * different sequences; each token attends causally to rows 0..pos[t] of its
- * sequence, which includes the rows this call writes.
+ * sequence, which includes the rows this call writes.  cap <= 8192.
  * ws: qk_layer_workspace(cfg, tokens) bytes. */
 int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t tokens,
                   const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,
                   void* ws, size_t ws_bytes, void* stream);
 
 size_t qk_layer_workspace(const qk_layer_cfg* cfg, int64_t tokens);
+
+/* Model head [GUIDE 2 figure: final RMSNorm, LM head, logits, greedy next
+ * token]: logits = W . Q8_0(rmsnorm(x, gamma)) with W [vocab][hidden] Q4_0,
+ * next[t] = argmax_i logits[t][i] (ties to the lowest index).
+ * x [tokens][hidden], gamma [hidden], logits [tokens][vocab] fp32, next int32
+ * [tokens].  ws: qk_lm_head_workspace() bytes. */
+int qk_lm_head(const float* x, const float* gamma, float eps, const uint8_t* w_q,
+               const uint16_t* w_d, int64_t vocab, int64_t hidden, int64_t tokens, float* logits,
+               int32_t* next, void* ws, size_t ws_bytes, void* stream);
+
+size_t qk_lm_head_workspace(int64_t vocab, int64_t hidden, int64_t tokens);
 
 /* ---------------------------------------------------------------------- */
 /* Mixture of experts                                                     */

@@ -68,6 +68,8 @@ _SIGS = {
     "moe_route_and_apply": ([_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
                              _SZ, _P], ctypes.c_int),
     "qk_moe_workspace": ([_I64, _I64, _I64, _I32, _I64], _SZ),
+    "qk_lm_head": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "qk_lm_head_workspace": ([_I64, _I64, _I64], _SZ),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -332,6 +334,25 @@ def layer_forward(w, cfg: LayerCfg, x, pos, seq, k_cache, v_cache, ws=None):
                                 _dev16(v_cache, "v_cache"), wsb.data_ptr(), need,
                                 _stream()), "layer_forward")
     return x
+
+
+def qk_lm_head_workspace(vocab: int, hidden: int, tokens: int) -> int:
+    return int(load().qk_lm_head_workspace(vocab, hidden, tokens))
+
+
+def qk_lm_head(x, gamma, eps: float, w_q, w_d, logits=None, next_ids=None, ws=None):
+    """logits [T][V] = W . Q8_0(rmsnorm(x)), next_ids [T] = greedy argmax."""
+    t, hidden = x.shape
+    vocab = w_q.shape[0]
+    lg = _out(logits, (t, vocab), torch.float32, x)
+    nx = _out(next_ids, (t,), torch.int32, x)
+    need = int(load().qk_lm_head_workspace(vocab, hidden, t))
+    wsb = _ws(ws, need, x.device)
+    _check(load().qk_lm_head(_dev(x, torch.float32, "x"), _dev(gamma, torch.float32, "gamma"), eps,
+                             _dev(w_q, torch.uint8, "w_q"), _dev16(w_d, "w_d"), vocab, hidden, t,
+                             _dev(lg, torch.float32, "logits"), _dev(nx, torch.int32, "next"),
+                             wsb.data_ptr(), need, _stream()), "qk_lm_head")
+    return lg, nx
 
 
 def qk_moe_workspace(tokens, hidden, n_experts, top_k, ffn) -> int:

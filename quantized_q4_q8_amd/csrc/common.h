@@ -25,18 +25,32 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 
 // ---------------------------------------------------------- wave reductions
 // Butterfly over groups of W adjacent lanes (W a power of two <= 64).
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
+template <int W, typename T>
+__device__ __forceinline__ T group_sum(T v) {
 #pragma unroll
     for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
     return v;
 }
-template <int W>
-__device__ __forceinline__ float group_max(float v) {
+template <int W, typename T>
+__device__ __forceinline__ T group_max(T v) {
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    for (int o = W / 2; o > 0; o >>= 1) {
+        const T u = __shfl_xor(v, o, WAVE);
+        v = u > v ? u : v;
+    }
     return v;
 }
+
+// Arithmetic precision.  Activations and outputs are stored as fp32, but
+// every floating-point reduction of the path (block-scaled matmul sums,
+// norms, softmax and attention sums, SwiGLU, router and combine) is carried
+// in fp64 and rounded to fp32 once, where the result is stored.  The Q8_0
+// quantization of activations is discontinuous (a value that moves across a
+// rounding boundary changes a whole code step), and over a stack of layers
+// such flips compound; computing each stored value to within an fp64
+// rounding of its exact value makes it equal to the correctly rounded fp32
+// result except in vanishingly rare midpoint cases, so the quantization
+// decisions follow the mathematical values and not the summation order.
 
 // ------------------------------------------------------------ Q8_0 helpers
 // Four adjacent lanes (lane % 4 == 0..3) hold the 32 values of one block,

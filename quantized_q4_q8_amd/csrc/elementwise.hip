@@ -6,7 +6,7 @@ namespace qk {
 
 // ---------------------------------------------------------------- RMSNorm
 // kenji.blog TinyLLaMA-in-C++ guide, section 4.1: y = x / sqrt(mean(x^2) +
-// eps) * gamma.  One workgroup per row.  Pass 1 sums squares (fp32, wave
+// eps) * gamma.  One workgroup per row.  Pass 1 sums squares (fp64, wave
 // butterflies then LDS across waves); pass 2 writes y and, when asked,
 // quantizes it to Q8_0 with the same arithmetic as quantize_q8_0 (each lane
 // holds 8 consecutive outputs, four lanes a block).
@@ -15,22 +15,22 @@ __global__ __launch_bounds__(256) void k_rmsnorm_q8(const float* __restrict__ x,
                                                     float eps, float* __restrict__ y,
                                                     int8_t* __restrict__ xq,
                                                     uint16_t* __restrict__ xd) {
-    __shared__ float red[4];
+    __shared__ double red[4];
     const int64_t row = blockIdx.x;
     const float* xr = x + row * dim;
-    float ss = 0.0f;
+    double ss = 0.0;
     for (int64_t i = threadIdx.x * 4; i < dim; i += 256 * 4) {
         const float4 v = *reinterpret_cast<const float4*>(xr + i);
-        ss = fmaf(v.x, v.x, ss);
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
+        ss = fma((double)v.x, (double)v.x, ss);
+        ss = fma((double)v.y, (double)v.y, ss);
+        ss = fma((double)v.z, (double)v.z, ss);
+        ss = fma((double)v.w, (double)v.w, ss);
     }
     ss = group_sum<WAVE>(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float total = red[0] + red[1] + red[2] + red[3];
-    const float inv = 1.0f / sqrtf(total / (float)dim + eps);
+    const double total = red[0] + red[1] + red[2] + red[3];
+    const double denom = sqrt(total / (double)dim + (double)eps);
     // pass 2: 8 values per lane; the loop bound keeps whole quads together
     for (int64_t i0 = 0; i0 < dim; i0 += 256 * 8) {
         const int64_t i = i0 + threadIdx.x * 8;
@@ -41,8 +41,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_q8(const float* __restrict__ x,
             const float4 b = *reinterpret_cast<const float4*>(xr + i + 4);
             const float4 ga = *reinterpret_cast<const float4*>(gamma + i);
             const float4 gb = *reinterpret_cast<const float4*>(gamma + i + 4);
-            v[0] = a.x * inv * ga.x; v[1] = a.y * inv * ga.y; v[2] = a.z * inv * ga.z; v[3] = a.w * inv * ga.w;
-            v[4] = b.x * inv * gb.x; v[5] = b.y * inv * gb.y; v[6] = b.z * inv * gb.z; v[7] = b.w * inv * gb.w;
+            const float xs[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const float gs[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (float)((double)xs[e] / denom * (double)gs[e]);
             if (y) {
                 *reinterpret_cast<float4*>(y + row * dim + i) = make_float4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<float4*>(y + row * dim + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -74,8 +76,8 @@ int launch_rmsnorm_q8(const float* x, const float* gamma, int64_t rows, int64_t 
 // ------------------------------------------------------------------- RoPE
 // kenji.blog TinyLLaMA-in-C++ guide, section 4.2: the adjacent pair
 // (x[2i], x[2i+1]) turns by m * theta_i, m the absolute position.  theta_i =
-// base^(-2i/hd); the angle, its reduction and cos/sin are taken in fp64 per
-// (token, pair) so that positions in the thousands keep full fp32 accuracy.
+// base^(-2i/hd); the angle, cos/sin and the rotation are taken in fp64 per
+// (token, pair) and the result rounded once to fp32.
 // One workgroup per token; q heads then k heads are rotated in place, after
 // which (when caches are given) k and v rows are stored to the fp16 KV cache
 // at row pos of the token's sequence (TinyLLaMA-in-C++ guide, section 7).
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(float* __restrict__ base, int64
                                                  const int32_t* __restrict__ seq, float rbase,
                                                  uint16_t* __restrict__ kc,
                                                  uint16_t* __restrict__ vc, int64_t cap) {
-    __shared__ float cs[2][256];
+    __shared__ double cs[2][256];
     const int64_t t = blockIdx.x;
     const int64_t half = hd / 2;
     const int p = pos[t];
@@ -94,8 +96,8 @@ __global__ __launch_bounds__(256) void k_rope_kv(float* __restrict__ base, int64
         const double theta = pow((double)rbase, -2.0 * (double)i / (double)hd);
         double sn, cn;
         sincos((double)p * theta, &sn, &cn);
-        cs[0][i] = (float)cn;
-        cs[1][i] = (float)sn;
+        cs[0][i] = cn;
+        cs[1][i] = sn;
     }
     __syncthreads();
     float* row = base + t * tok_stride;
@@ -104,8 +106,9 @@ __global__ __launch_bounds__(256) void k_rope_kv(float* __restrict__ base, int64
         const int64_t hh = idx / half, i = idx % half;
         float* xp = hh < nq ? row + q_off + hh * hd + 2 * i : row + k_off + (hh - nq) * hd + 2 * i;
         const float2 v = *reinterpret_cast<float2*>(xp);
-        const float c = cs[0][i], sn = cs[1][i];
-        const float2 o = make_float2(v.x * c - v.y * sn, v.x * sn + v.y * c);
+        const double c = cs[0][i], sn = cs[1][i];
+        const double x1 = v.x, x2 = v.y;
+        const float2 o = make_float2((float)(x1 * c - x2 * sn), (float)(x1 * sn + x2 * c));
         *reinterpret_cast<float2*>(xp) = o;
         if (kc && hh >= nq && p >= 0 && p < cap) {
             const int64_t g = hh - nq;
@@ -157,8 +160,8 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ g,
                                                 float* __restrict__ h) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const float z = g[i];
-    h[i] = z / (1.0f + expf(-z)) * u[i];
+    const double z = g[i];
+    h[i] = (float)(z / (1.0 + exp(-z)) * (double)u[i]);
 }
 
 // -------------------------------------------------------------- embedding

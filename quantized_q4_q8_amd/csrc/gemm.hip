@@ -5,7 +5,7 @@
 // every 32-element block contributes delta_w * delta_x * (exact int32 dot).
 // One MFMA with K = 32 covers exactly one block, so its int32 result is the
 // block dot of a 32 x 32 tile of (token, weight row) pairs; the two scales
-// are applied in fp32 right after it.
+// are applied right after it and the scaled block dots are summed in fp64.
 //
 // Tile: a workgroup (4 waves) computes 128 tokens x 128 weight rows; each
 // wave 64 x 64 as 2 x 2 MFMA tiles.  Activations are the MFMA's A operand
@@ -38,7 +38,11 @@ struct __align__(16) Stage {
     float db[KB][BR];           // weight scales
 };
 
-__device__ __forceinline__ float swish(float z) { return z / (1.0f + expf(-z)); }
+// swish(g) * u of fp32 matmul outputs, in fp64, rounded once
+__device__ __forceinline__ float swiglu1(float g, float u) {
+    const double gd = (double)g;
+    return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+}
 
 }  // namespace
 
@@ -125,13 +129,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
         }
     };
 
-    float acc[2][2][16];
+    double acc[2][2][16];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0;
 
     // LDS row (weights) of column tile cb for this wave
     auto lds_col = [&](int cb) -> int {
@@ -182,8 +186,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
                 for (int cb = 0; cb < 2; ++cb) {
                     const v16i isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[ta], wb[cb], zero, 0, 0, 0);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        acc[ta][cb][v] = fmaf(dxa[v] * dwl[cb], (float)isum[v], acc[ta][cb][v]);
+                    for (int v = 0; v < 16; ++v)   // scale product exact in fp32, term exact in fp64
+                        acc[ta][cb][v] = fma((double)(dxa[v] * dwl[cb]), (double)isum[v], acc[ta][cb][v]);
                 }
             }
         }
@@ -207,13 +211,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
                     const int pr = lds_col(cb);
                     if (!prow_valid(pr)) continue;
                     const int64_t r = prow_of(pr);
-                    float val = acc[ta][cb][v];
-                    if (a.residual) val += a.residual[t * a.ldr + r];
+                    float val = (float)acc[ta][cb][v];
+                    if (a.residual) val = a.residual[t * a.ldr + r] + val;
                     a.y[t * a.ldy + r] = val;
                 }
             } else {
                 const int64_t f = c0 + wc * 32 + j;
-                if (f < a.ffn) a.y[t * a.ldy + f] = swish(acc[ta][0][v]) * acc[ta][1][v];
+                if (f < a.ffn) a.y[t * a.ldy + f] = swiglu1((float)acc[ta][0][v], (float)acc[ta][1][v]);
             }
         }
     }

@@ -8,6 +8,14 @@ namespace qk {
 enum GemvEpilogue : int {
     EPI_STORE = 0,   // y = acc (+ residual)
     EPI_SWIGLU = 1,  // rows f and f + ffn are gate and up: y[f] = swish(gate) * up
+    EPI_QKV = 2,     // RoPE on q and k row pairs; q -> q_out, k and v -> fp16 caches
+    EPI_ARGMAX = 3,  // y = acc, plus each workgroup's (max, lowest index) per column
+};
+
+enum GemvPrologue : int {
+    PRO_NONE = 0,     // activations read as Q8_0 (xq, xd) from global memory
+    PRO_RMSNORM = 1,  // activations = Q8_0(rmsnorm(xf, gamma)), built in LDS per workgroup
+    PRO_Q8 = 2,       // activations = Q8_0(xf), built in LDS per workgroup
 };
 
 // A (possibly grouped) Q4_0 x Q8_0 product.  Group g (blockIdx.y) uses the
@@ -33,9 +41,36 @@ struct GemvArgs {
     int64_t ldr;
     int64_t ffn;             // EPI_SWIGLU: gate rows [0, ffn), up rows [ffn, 2 ffn)
     int32_t max_cols;        // upper bound of columns per group (picks the tile)
+    // prologue (PRO_RMSNORM / PRO_Q8): fp32 activations [rows][k], gain, eps
+    const float* xf;
+    const float* gamma;
+    float eps;
+    // EPI_QKV: rows [0, q_rows) are q, then kv_rows of k, then kv_rows of v;
+    // head_dim hd, n_kv heads, caches [seqs][n_kv][cap][hd]; q_out [m][q_rows]
+    int64_t q_rows, kv_rows, hd, n_kv, cap;
+    float rope_base;
+    const int32_t* pos;
+    const int32_t* seq;
+    uint16_t* kc;
+    uint16_t* vc;
+    float* q_out;
+    // EPI_ARGMAX: partials [column][workgroup]
+    float* part_val;
+    int32_t* part_idx;
+    // workgroup (0, 0) zeroes zero_n words at zero_ptr (counters of a later kernel)
+    int32_t* zero_ptr;
+    int32_t zero_n;
 };
 
-int launch_gemv(const GemvArgs& a, int epi, hipStream_t s);
+// Launch the GEMV with the given epilogue and prologue; returns QK_ESHAPE when
+// the prologue's LDS staging would not fit (the caller then stages itself).
+int launch_gemv(const GemvArgs& a, int epi, hipStream_t s, int pro = PRO_NONE);
+bool gemv_prologue_fits(int64_t k, int64_t max_cols);
+
+// Final step of EPI_ARGMAX: idx[c] = index of the best partial of column c.
+int launch_argmax_partials(const float* part_val, const int32_t* part_idx, int64_t nparts,
+                           int64_t cols, int32_t* idx, hipStream_t s);
+int64_t gemv_argmax_parts(int64_t n, int64_t k, int64_t max_cols);
 
 // Q8_0 of [rows][k] fp32 (k % 32 == 0).
 int launch_quantize_q8(const float* x, int64_t rows, int64_t k, int8_t* xq, uint16_t* xd,
@@ -57,11 +92,16 @@ int launch_rope_kv(float* base, int64_t tokens, int64_t tok_stride, int64_t q_of
                    const int32_t* seq, float rope_base, uint16_t* k_cache, uint16_t* v_cache,
                    int64_t cap, hipStream_t s);
 
-// Attention with explicit q/out token strides (elements).
+// Attention with explicit q/out token strides (elements): a chunk kernel and a
+// merge kernel.  The merge writes fp32 `out` (when non-null) and/or the Q8_0
+// of the output row (oq, od; when non-null, with out_tok_stride also the Q8_0
+// row length).  `counters_zeroed` is unused (no counters).
 int launch_attention(const float* q, int64_t q_tok_stride, int64_t tokens, int64_t nq,
                      int64_t nkv, int64_t hd, const uint16_t* kc, const uint16_t* vc, int64_t cap,
                      const int32_t* pos, const int32_t* seq, float* out, int64_t out_tok_stride,
-                     void* ws, size_t ws_bytes, hipStream_t s);
-size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t hd, int64_t cap);
+                     int8_t* oq, uint16_t* od, void* ws, size_t ws_bytes, bool counters_zeroed,
+                     hipStream_t s);
+size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t nkv, int64_t hd, int64_t cap);
+int64_t attention_counter_words(int64_t tokens, int64_t nkv);
 
 }  // namespace qk

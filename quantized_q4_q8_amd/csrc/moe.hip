@@ -8,8 +8,8 @@
 // TinyLLaMA-in-C++ guide, section 4.4).
 //
 // Pipeline (all on the caller's stream, deterministic, no float atomics):
-//  1. router logits r = x . W_r, H split into slices whose partial sums are
-//     added in a fixed order;
+//  1. router logits r = x . W_r in fp64, H split into slices whose partial
+//     sums are added in a fixed order, rounded to fp32;
 //  2. per token: top-k on r (ties to the lower expert), sigmoid scores,
 //     weights normalized over the selection;
 //  3. stable counting sort of the (token, rank) pairs by expert -> per-expert
@@ -29,7 +29,7 @@ constexpr int RSLICE = 768;  // hidden elements per router slice
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct MoeWs {
-    float* rpart;       // [slices][T][E]
+    double* rpart;      // [slices][T][E]
     int32_t* off;       // [E + 1]
     int32_t* col_tok;   // [P] token of each sorted column
     int32_t* slot;      // [P] sorted column of pair p = t * k + rank
@@ -52,7 +52,7 @@ MoeWs moe_layout(void* base, int64_t T, int64_t H, int64_t E, int64_t k, int64_t
         o = align256(o + bytes);
         return base ? static_cast<char*>(base) + at : nullptr;
     };
-    w.rpart = reinterpret_cast<float*>(take(sizeof(float) * slices * T * E));
+    w.rpart = reinterpret_cast<double*>(take(sizeof(double) * slices * T * E));
     w.off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
     w.col_tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
     w.slot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
@@ -71,7 +71,7 @@ MoeWs moe_layout(void* base, int64_t T, int64_t H, int64_t E, int64_t k, int64_t
 // rpart[s][t][e] = sum over h in slice s of x[t][h] * W_r[h][e]; thread = expert.
 __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int64_t T, int64_t H,
                                                 const float* __restrict__ wr, int64_t E,
-                                                float* __restrict__ rpart) {
+                                                double* __restrict__ rpart) {
     __shared__ float xs[RT][RSLICE];
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.y * RT;
@@ -84,13 +84,13 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
     }
     __syncthreads();
     if (e >= E) return;
-    float acc[RT];
+    double acc[RT];
 #pragma unroll
-    for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0f;
+    for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0;
     for (int64_t hh = 0; hh < hn; ++hh) {
-        const float w = wr[(h0 + hh) * E + e];
+        const double w = wr[(h0 + hh) * E + e];
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) acc[tt] = fmaf(xs[tt][hh], w, acc[tt]);
+        for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][hh], w, acc[tt]);
     }
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt)
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
 // One workgroup (256 threads) per token: r[e] from the slices in order, then
 // top-k by repeated (value, lowest index) maxima over the experts not yet
 // taken (NaN never wins), then sigmoid weights normalized over the choice.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ rpart, int64_t slices,
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ rpart, int64_t slices,
                                               int64_t T, int64_t E, int32_t k,
                                               int32_t* __restrict__ sel_idx,
                                               float* __restrict__ sel_w) {
@@ -111,9 +111,9 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ rpart, i
     __shared__ int chosen_e[32];
     const int64_t t = blockIdx.x;
     for (int64_t e = threadIdx.x; e < E; e += 256) {
-        float r = 0.0f;
+        double r = 0.0;
         for (int64_t s = 0; s < slices; ++s) r += rpart[(s * T + t) * E + e];
-        rv[e] = r;
+        rv[e] = (float)r;
         taken[e] = 0;
     }
     __syncthreads();
@@ -145,15 +145,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ rpart, i
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        float ssum = 0.0f;
-        float sv[32];
+        double ssum = 0.0;
+        for (int kk = 0; kk < k; ++kk) ssum += 1.0 / (1.0 + exp(-(double)rv[chosen_e[kk]]));
         for (int kk = 0; kk < k; ++kk) {
-            sv[kk] = 1.0f / (1.0f + expf(-rv[chosen_e[kk]]));
-            ssum += sv[kk];
-        }
-        for (int kk = 0; kk < k; ++kk) {
+            const double sv = 1.0 / (1.0 + exp(-(double)rv[chosen_e[kk]]));
             sel_idx[t * k + kk] = chosen_e[kk];
-            sel_w[t * k + kk] = sv[kk] / ssum;
+            sel_w[t * k + kk] = (float)(sv / ssum);
         }
     }
 }
@@ -213,10 +210,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ys, i
     const int64_t t = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= H) return;
-    float acc = 0.0f;
+    double acc = 0.0;
     for (int r = 0; r < k; ++r)
-        acc = fmaf(sel_w[t * k + r], ys[(int64_t)slot[t * k + r] * H + i], acc);
-    out[t * H + i] = acc;
+        acc = fma((double)sel_w[t * k + r], (double)ys[(int64_t)slot[t * k + r] * H + i], acc);
+    out[t * H + i] = (float)acc;
 }
 
 }  // namespace qk

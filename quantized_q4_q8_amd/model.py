@@ -13,8 +13,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (LayerWeights, Workspace, layer_cfg, layer_forward, qk_argmax, qk_embed_lookup,
-               qk_layer_workspace, qk_quantize_q4_0, qmatmul_q4_0_q8_0, quantize_q8_0, rmsnorm)
+from . import (LayerWeights, Workspace, layer_cfg, layer_forward, qk_embed_lookup,
+               qk_layer_workspace, qk_lm_head, qk_lm_head_workspace, qk_quantize_q4_0)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -75,11 +75,13 @@ class Decoder:
         self.k_cache = torch.zeros(kv_shape, dtype=torch.int16, device=device)
         self.v_cache = torch.zeros(kv_shape, dtype=torch.int16, device=device)
         self.ws = Workspace()
+        self.head_ws = Workspace()
         self.device = device
 
     def reserve(self, tokens: int) -> None:
         """Size the workspace for calls of up to `tokens` tokens (before graph capture)."""
         self.ws.reserve(qk_layer_workspace(self.cfg, tokens), self.device)
+        self.head_ws.reserve(qk_lm_head_workspace(self.s.vocab, self.s.hidden, tokens), self.device)
 
     def hidden_states(self, ids: torch.Tensor, pos: torch.Tensor, seq: torch.Tensor,
                       x: torch.Tensor | None = None) -> torch.Tensor:
@@ -89,28 +91,17 @@ class Decoder:
             layer_forward(st, self.cfg, x, pos, seq, self.k_cache[li], self.v_cache[li], ws=self.ws)
         return x
 
-    def logits(self, x: torch.Tensor, out: torch.Tensor | None = None,
-               scratch: dict | None = None) -> torch.Tensor:
-        sc = scratch if scratch is not None else {}
-        xn = rmsnorm(x, self.gamma_final, self.s.eps, out=sc.get("xn"))
-        xq, xd = quantize_q8_0(xn, out_q=sc.get("xq"), out_d=sc.get("xd"))
-        return qmatmul_q4_0_q8_0(self.lm_q, self.lm_d, xq, xd, out=out)
-
     def step(self, ids: torch.Tensor, pos: torch.Tensor, seq: torch.Tensor,
              bufs: dict | None = None) -> tuple[torch.Tensor, torch.Tensor]:
         """One forward over ids [T]: returns (logits [T][V], argmax ids [T])."""
         b = bufs if bufs is not None else {}
         x = self.hidden_states(ids, pos, seq, x=b.get("x"))
-        lg = self.logits(x, out=b.get("logits"), scratch=b)
-        nxt = qk_argmax(lg, out=b.get("next"))
-        return lg, nxt
+        return qk_lm_head(x, self.gamma_final, self.s.eps, self.lm_q, self.lm_d,
+                          logits=b.get("logits"), next_ids=b.get("next"), ws=self.head_ws)
 
     def step_buffers(self, tokens: int) -> dict:
         """Preallocated buffers so that `step` allocates nothing (graph capture)."""
         dev, H, V = self.device, self.s.hidden, self.s.vocab
         return dict(x=torch.empty((tokens, H), dtype=torch.float32, device=dev),
-                    xn=torch.empty((tokens, H), dtype=torch.float32, device=dev),
-                    xq=torch.empty((tokens, H), dtype=torch.int8, device=dev),
-                    xd=torch.empty((tokens, H // 32), dtype=torch.int16, device=dev),
                     logits=torch.empty((tokens, V), dtype=torch.float32, device=dev),
                     next=torch.empty((tokens,), dtype=torch.int32, device=dev))

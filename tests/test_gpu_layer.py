@@ -7,7 +7,7 @@ import oracle
 import synth
 from quantized_q4_q8_amd.model import layer_to_device
 from synth import workloads as W
-from tests.util import LAYER_TOL, dev, host, rel_err, say
+from tests.util import LAYER_TOL, assert_same_fp32, dev, host, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,8 @@ def test_layer_small_prefill_then_self_fed_decode(gpu_lib):
     xg = dev(x)
     qk.layer_forward(lw, cfg, xg, dev(pos), dev(seq), kcg, vcg)
     assert rel_err(host(xg), ref) < LAYER_TOL
+    assert_same_fp32(host(xg), ref)
+    assert np.mean(host(kcg, np.uint16) == kc) > 0.999
     kf = oracle.f16_to_f32(kc)
     assert rel_err(oracle.f16_to_f32(host(kcg, np.uint16)), kf) < LAYER_TOL
     o_in, g_in = ref[-1:], host(xg)[-1:]
@@ -62,6 +64,7 @@ def test_layer_small_prefill_then_self_fed_decode(gpu_lib):
         qk.layer_forward(lw, cfg, xs, dev(p), dev(s0), kcg, vcg)
         g_out = host(xs)
         assert rel_err(g_out, o_out) < LAYER_TOL, f"decode step {step}"
+        assert_same_fp32(g_out, o_out)
         o_in, g_in = o_out, g_out
 
 
@@ -86,6 +89,7 @@ def test_layer_ragged_sequences(gpu_lib, tokens):
     xg = dev(x)
     qk.layer_forward(lw, qk.layer_cfg(**g.cfg(cap)), xg, dev(pos), dev(seq), kcg, vcg)
     assert rel_err(host(xg), ref) < LAYER_TOL
+    assert_same_fp32(host(xg), ref)
 
 
 def test_layer_decode_equals_prefill_last_row(gpu_lib):
@@ -151,6 +155,7 @@ def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     check_routing(sel_g, w_g, sel, w, logits)
     if np.array_equal(sel_g, sel):
         assert rel_err(host(y), out) < LAYER_TOL
+        assert_same_fp32(host(y), out)
     # every selection is a set of distinct experts and weights sum to 1
     assert all(len(set(r)) == k for r in sel_g)
     assert np.allclose(w_g.sum(1), 1.0, atol=1e-6)

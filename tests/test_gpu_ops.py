@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 from synth import workloads as W
-from tests.util import LAYER_TOL, dev, host, rel_err, say
+from tests.util import LAYER_TOL, assert_same_fp32, dev, host, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,7 @@ def test_qmatmul_matches_oracle(gpu_lib, n, k, m):
     y = qk.qmatmul_q4_0_q8_0(dev(wq), dev(wd), dev(xq), dev(xd))
     ref = oracle.qmatmul(wq, wd, xq, xd)
     assert rel_err(host(y), ref) < 1e-5
+    assert_same_fp32(host(y), ref)
 
 
 @pytest.mark.parametrize("ffn,k,m", [(5632, 2048, 1), (704, 256, 16), (96, 64, 5), (2048, 6144, 3)])
@@ -109,6 +110,7 @@ def test_gate_up_swiglu(gpu_lib, ffn, k, m):
     gu = oracle.qmatmul(wq, wd, xq, xd)
     ref = oracle.swiglu(gu[:, :ffn], gu[:, ffn:])
     assert rel_err(host(h), ref) < 1e-5
+    assert_same_fp32(host(h), ref)
 
 
 def test_qmatmul_zero_and_empty(gpu_lib):
@@ -134,6 +136,7 @@ def test_rmsnorm(gpu_lib, rows, dim):
     g = synth.normal(106, 1, dim, 0.02, mean=1.0)
     y = qk.rmsnorm(dev(x), dev(g), 1e-5)
     assert rel_err(host(y), oracle.rmsnorm(x, g, 1e-5)) < 2e-6
+    assert_same_fp32(host(y), oracle.rmsnorm(x, g, 1e-5))
 
 
 @pytest.mark.parametrize("tokens,heads,hd", [(16, 12, 32), (3, 36, 64), (1, 1, 2)])
@@ -148,6 +151,7 @@ def test_rope(gpu_lib, tokens, heads, hd):
     got = host(xg)
     assert np.array_equal(got[0], x[0])       # position 0 is the identity
     assert rel_err(got, ref) < 2e-6
+    assert_same_fp32(got, ref)
 
 
 def test_swiglu(gpu_lib):
@@ -157,6 +161,7 @@ def test_swiglu(gpu_lib):
     u = synth.normal(108, 1, 5000)
     h = qk.swiglu(dev(g), dev(u))
     assert rel_err(host(h), oracle.swiglu(g, u)) < 2e-6
+    assert_same_fp32(host(h), oracle.swiglu(g, u))
 
 
 def test_kv_append_bit_exact(gpu_lib):
@@ -232,6 +237,7 @@ def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
     out = qk.gqa_attention(dev(q), dev(kc), dev(vc), dev(pos), dev(seq))
     ref = oracle.gqa_attention(q, kc, vc, pos, seq)
     assert rel_err(host(out), ref) < 1e-5
+    assert_same_fp32(host(out), ref)
 
 
 # ---------------------------------------------------------------- errors

@@ -17,6 +17,26 @@ def rel_err(got, want) -> float:
     return float(np.max(np.abs(got - want) / den))
 
 
+def ulp_diff(got, want) -> np.ndarray:
+    """Distance in fp32 units in the last place (same-sign finite values)."""
+    g = np.asarray(got, np.float32).view(np.int32).astype(np.int64)
+    w = np.asarray(want, np.float32).view(np.int32).astype(np.int64)
+    g = np.where(g < 0, np.int64(-2**31) - g, g)
+    w = np.where(w < 0, np.int64(-2**31) - w, w)
+    return np.abs(g - w)
+
+
+def assert_same_fp32(got, want, min_equal=0.999, max_ulp=2):
+    """The GPU carries its sums in fp64 and rounds once, so its fp32 values
+    should equal the oracle's except for rare rounding-midpoint cases."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    eq = float(np.mean(got == want)) if want.size else 1.0
+    worst = int(ulp_diff(got, want).max()) if want.size else 0
+    assert eq >= min_equal and worst <= max_ulp, f"equal fraction {eq:.6f}, worst {worst} ulp"
+    return eq
+
+
 def dev(a, device="cuda"):
     import torch
     a = np.ascontiguousarray(a)
