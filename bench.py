@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
-    ap.add_argument("--kernel-rounds", type=int, default=5)
+    ap.add_argument("--kernel-rounds", type=int, default=20)
+    ap.add_argument("--decode-tokens", type=int, default=128,
+                    help="tokens per step; only for short profiling runs (the workload is 128)")
     return ap.parse_args()
 
 
@@ -145,7 +147,8 @@ def run_decode(args):
     from synth import workloads as W
 
     spec = W.DECODE
-    g, L, steps_per_run = spec["geometry"], spec["layers"], spec["steps"]
+    g, L = spec["geometry"], spec["layers"]
+    steps_per_run = max(1, min(args.decode_tokens, spec["steps"]))
     want_cpu = not args.no_cpu_baseline
     dec, first, host = build_decoder(spec, want_cpu)
     dev = dec.device
@@ -189,33 +192,47 @@ def run_decode(args):
     tok_s = steps_per_run * args.steps / (ms / 1e3)
     log(f"decode: {ms_per_step:.3f} ms per {steps_per_run}-token step, {tok_s:.1f} tok/s")
 
-    # -- the dominant kernel on its own: gate/up + SwiGLU GEMV of every layer
-    #    in turn (the 22 layers' 285 MB exceed the 256 MB MALL), one pair of
-    #    HIP events around each launch on the launching stream
+    # -- the dominant kernel on its own: the fused RMSNorm + Q8_0 + gate/up +
+    #    SwiGLU GEMV (the same kernel instance the decode step runs), once per
+    #    layer in turn (the 22 layers' 286 MB exceed the 256 MB MALL),
+    #    back-to-back in one captured graph; HIP events on the replay stream
     x = normal(7, 0, (1, g.hidden))
-    xq, xd = qk.quantize_q8_0(torch.from_numpy(x).to(dev))
+    xg = torch.from_numpy(x).to(dev)
     h = torch.empty((1, g.ffn_padded), dtype=torch.float32, device=dev)
-    for lw in dec.layers:
-        qk.qk_gate_up_swiglu(lw.w_gate_up_q, lw.w_gate_up_d, xq, xd, out=h)
-    evs = []
-    for _ in range(args.kernel_rounds):
+    def ffn_ups():
         for lw in dec.layers:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            qk.qk_gate_up_swiglu(lw.w_gate_up_q, lw.w_gate_up_d, xq, xd, out=h)
-            b.record()
-            evs.append((a, b))
+            qk.qk_ffn_up(xg, lw.gamma_ffn, g.eps, lw.w_gate_up_q, lw.w_gate_up_d, out=h)
+    ffn_ups()
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e3 for a, b in evs]          # microseconds
-    avg_us = float(np.mean(durs))
+    kg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kg):
+        ffn_ups()
+    kg.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.kernel_rounds):
+        kg.replay()
+    b.record()
+    torch.cuda.synchronize()
+    avg_us = a.elapsed_time(b) * 1e3 / (args.kernel_rounds * L)
     H, F = g.hidden, g.ffn_padded
-    kbytes = 2 * F * H * 9 / 16 + H + (H // 32) * 2 + F * 4   # weights + Q8_0 x + h out
+    # weights, Q4_0; x and gamma fp32 read; h fp32 written
+    kbytes = 2 * F * H * 9 / 16 + 2 * H * 4 + F * 4
     achieved = kbytes / (avg_us * 1e-6) / 1e9
-    kname = "k_gemv<1,64,4,4,EPI_SWIGLU>"
+    kname = "k_gemv<1,64,4,1,EPI_SWIGLU,PRO_RMSNORM,1>"
     src = source_hash([os.path.join(ROOT, "quantized_q4_q8_amd", "csrc", f)
                        for f in ("gemv.hip", "internal.h", "common.h")])
     traffic = stored_traffic(kname, src)
-    log(f"gate/up GEMV: {avg_us:.2f} us per launch, {achieved:.0f} GB/s")
+    log(f"fused gate/up GEMV: {avg_us:.2f} us per launch, {achieved:.0f} GB/s")
+
+    # -- a plain 256 MiB device copy: calibrates the HBM byte counters
+    #    (FETCH_SIZE / WRITE_SIZE) of profiling runs against a known size
+    cal_src = torch.empty(64 * 2**20, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     step_bytes = decode_bytes_per_token(spec)
     out = {
@@ -229,7 +246,7 @@ def run_decode(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 x q8_0 (int32 block dots, fp32 accumulate)",
+        "dtype": "q4_0 x q8_0 (int32 block dots, fp64 accumulate, fp32 activations)",
         "data": "synthetic: seeded N(0,0.02) Q4_0 weights, N(0,1) fp16 KV prefill",
         "config": {"workload": "tinyllama-1.1b-shape greedy decode, 22 layers, context 2048->2175",
                    "tokens_per_step": steps_per_run, "batch": 1, "layers": L,
@@ -239,7 +256,8 @@ def run_decode(args):
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": int(kbytes),
-                     "avg_us": round(avg_us, 3)},
+                     "avg_us": round(avg_us, 3), "launches_timed": args.kernel_rounds * L,
+                     "source_hash": src},
         "step_roofline": {"bytes_per_token": int(step_bytes),
                           "achieved_GBps": round(step_bytes * tok_s / 1e9, 1),
                           "frac": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),

@@ -220,6 +220,17 @@ int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t 
 
 size_t qk_layer_workspace(const qk_layer_cfg* cfg, int64_t tokens);
 
+/* First half of the feed-forward block [GUIDE 4.1, 4.4]:
+ * h = SwiGLU(W_gate . Q8_0(u), W_up . Q8_0(u)), u = rmsnorm(x, gamma), with
+ * W [2 ffn][hidden] Q4_0 (gate rows, then up rows).  x [tokens][hidden],
+ * gamma [hidden], h [tokens][ffn] fp32.  ws: qk_ffn_up_workspace() bytes
+ * (unused, and may be NULL, for tokens <= 8). */
+int qk_ffn_up(const float* x, const float* gamma, float eps, const uint8_t* w_q,
+              const uint16_t* w_d, int64_t ffn, int64_t hidden, int64_t tokens, float* h,
+              void* ws, size_t ws_bytes, void* stream);
+
+size_t qk_ffn_up_workspace(int64_t hidden, int64_t tokens);
+
 /* Model head [GUIDE 2 figure: final RMSNorm, LM head, logits, greedy next
  * token]: logits = W . Q8_0(rmsnorm(x, gamma)) with W [vocab][hidden] Q4_0,
  * next[t] = argmax_i logits[t][i] (ties to the lowest index).

@@ -70,6 +70,8 @@ _SIGS = {
     "qk_moe_workspace": ([_I64, _I64, _I64, _I32, _I64], _SZ),
     "qk_lm_head": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "qk_lm_head_workspace": ([_I64, _I64, _I64], _SZ),
+    "qk_ffn_up": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
+    "qk_ffn_up_workspace": ([_I64, _I64], _SZ),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -334,6 +336,20 @@ def layer_forward(w, cfg: LayerCfg, x, pos, seq, k_cache, v_cache, ws=None):
                                 _dev16(v_cache, "v_cache"), wsb.data_ptr(), need,
                                 _stream()), "layer_forward")
     return x
+
+
+def qk_ffn_up(x, gamma, eps: float, w_q, w_d, out=None, ws=None):
+    """h [T][ffn] = SwiGLU(W_gate . Q8_0(rmsnorm(x)), W_up . Q8_0(rmsnorm(x)))."""
+    t, hidden = x.shape
+    ffn = w_q.shape[0] // 2
+    h = _out(out, (t, ffn), torch.float32, x)
+    need = int(load().qk_ffn_up_workspace(hidden, t))
+    wsb = _ws(ws, need, x.device)
+    _check(load().qk_ffn_up(_dev(x, torch.float32, "x"), _dev(gamma, torch.float32, "gamma"), eps,
+                            _dev(w_q, torch.uint8, "w_q"), _dev16(w_d, "w_d"), ffn, hidden, t,
+                            _dev(h, torch.float32, "h"), wsb.data_ptr(), need, _stream()),
+           "qk_ffn_up")
+    return h
 
 
 def qk_lm_head_workspace(vocab: int, hidden: int, tokens: int) -> int:

@@ -170,6 +170,40 @@ extern "C" int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* 
     return layer_prefill(w, c, x, tokens, pos, seq, k_cache, v_cache, L, s);
 }
 
+// ------------------------------------------------------------- FFN first half
+// kenji.blog TinyLLaMA-in-C++ guide, sections 4.1 and 4.4: h = SwiGLU of the
+// gate and up projections of the RMSNorm'd input, each projection reading the
+// Q8_0 of that input.
+
+extern "C" size_t qk_ffn_up_workspace(int64_t hidden, int64_t tokens) {
+    if (hidden <= 0 || tokens < 0) return 0;
+    return align256((size_t)(tokens * hidden)) + align256(sizeof(uint16_t) * tokens * (hidden / QBLK));
+}
+
+extern "C" int qk_ffn_up(const float* x, const float* gamma, float eps, const uint8_t* w_q,
+                         const uint16_t* w_d, int64_t ffn, int64_t hidden, int64_t tokens,
+                         float* h, void* ws, size_t ws_bytes, void* stream) {
+    QK_REQUIRE(ffn > 0 && hidden > 0 && tokens >= 0 && tokens <= INT32_MAX, QK_EINVAL);
+    QK_REQUIRE(hidden % QBLK == 0 && ffn % QBLK == 0, QK_ESHAPE);
+    if (tokens == 0) return QK_OK;
+    QK_REQUIRE(x && gamma && w_q && w_d && h, QK_EINVAL);
+    QK_REQUIRE(QK_ALIGNED(x, 16) && QK_ALIGNED(gamma, 16) && QK_ALIGNED(w_q, 16) &&
+                   QK_ALIGNED(h, 4),
+               QK_EALIGN);
+    hipStream_t s = (hipStream_t)stream;
+    if (tokens <= 8 && gemv_prologue_fits(hidden, tokens)) {
+        GemvArgs a = plain(w_q, w_d, 2 * ffn, hidden, tokens);
+        a.xf = x; a.gamma = gamma; a.eps = eps; a.y = h; a.ldy = ffn; a.ffn = ffn;
+        return launch_gemv(a, EPI_SWIGLU, s, PRO_RMSNORM);
+    }
+    QK_REQUIRE(ws && ws_bytes >= qk_ffn_up_workspace(hidden, tokens), QK_EWORKSPACE);
+    int8_t* xq = static_cast<int8_t*>(ws);
+    uint16_t* xd = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align256((size_t)(tokens * hidden)));
+    int rc = launch_rmsnorm_q8(x, gamma, tokens, hidden, eps, nullptr, xq, xd, s);
+    if (rc) return rc;
+    return matmul(w_q, w_d, 2 * ffn, hidden, xq, xd, tokens, h, nullptr, EPI_SWIGLU, ffn, s);
+}
+
 // ---------------------------------------------------------------- LM head
 // kenji.blog TinyLLaMA-in-C++ guide, section 2 (pipeline figure): the last
 // hidden state goes through RMSNorm and the LM head to the logits, and the

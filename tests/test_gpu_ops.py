@@ -113,6 +113,21 @@ def test_gate_up_swiglu(gpu_lib, ffn, k, m):
     assert_same_fp32(host(h), ref)
 
 
+@pytest.mark.parametrize("ffn,hidden,tokens", [(5632, 2048, 1), (704, 256, 3), (96, 128, 20)])
+def test_ffn_up(gpu_lib, ffn, hidden, tokens):
+    qk = gpu_lib
+    say(f"qk_ffn_up ffn={ffn} hidden={hidden} tokens={tokens}")
+    x = synth.normal(114, 1, (tokens, hidden))
+    g = synth.normal(114, 2, hidden, 0.02, mean=1.0)
+    wq, wd = oracle.quantize_q4_0(synth.normal(114, 3, (2 * ffn, hidden), 0.02))
+    xq, xd = oracle.quantize_q8_0(oracle.rmsnorm(x, g, 1e-5))
+    gu = oracle.qmatmul(wq, wd, xq, xd)
+    ref = oracle.swiglu(gu[:, :ffn], gu[:, ffn:])
+    h = qk.qk_ffn_up(dev(x), dev(g), 1e-5, dev(wq), dev(wd))
+    assert rel_err(host(h), ref) < 1e-5
+    assert_same_fp32(host(h), ref)
+
+
 def test_qmatmul_zero_and_empty(gpu_lib):
     qk = gpu_lib
     say("qmatmul zero weights, m = 0")
