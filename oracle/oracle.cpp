@@ -34,8 +34,9 @@
  *
  * Parity pins: every function here is checked by the CPU test suite against
  * closed forms, invariants, numpy's IEEE binary16 conversion or fp64 brute
- * force.  Parity unpinned: none of the functions; the only unpinned parts are
- * the GPU's fp32 accumulation orders, which the tolerances cover.
+ * force.  Parity unpinned: none of the functions.  Greedy tokens where the
+ * top-2 logit gap is within the logit tolerance are not pinned (either token
+ * is a correct greedy choice there).
  */
 #include <algorithm>
 #include <cmath>
