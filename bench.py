@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "matmul", "prefill", "moe"],
+                    help="decode (the headline line); the others measure the standalone matmul, "
+                         "prefill and MoE workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -73,7 +75,7 @@ def stored_traffic(kernel: str, src_hash: str):
 # ---------------------------------------------------------------------------
 # decode workload
 # ---------------------------------------------------------------------------
-def build_decoder(spec, want_host_q4: bool):
+def build_decoder(spec, want_host_q4: bool, seqs: int = 1):
     import numpy as np
     import torch
 
@@ -83,12 +85,11 @@ def build_decoder(spec, want_host_q4: bool):
     from synth import workloads as W
 
     g, seed, L, V, cap = spec["geometry"], spec["seed"], spec["layers"], spec["vocab"], spec["cap"]
-    ctx = spec["context"]
+    ctx = spec.get("context", 0)       # rows of the KV cache prefilled with N(0,1)
     host = {"layers": [], "kv": []} if want_host_q4 else None
     if want_host_q4:
         import oracle
     layers = []
-    kshape = (L, 1, g.n_kv_heads, cap, g.head_dim)
     t0 = time.time()
     for li in range(L):
         wf = W.layer_weights_f32(seed, li, g)
@@ -107,10 +108,10 @@ def build_decoder(spec, want_host_q4: bool):
     lm = normal(seed, W.TID_LM_HEAD, (V, g.hidden), W.WEIGHT_STD)
     lm_q, lm_d = qk.qk_quantize_q4_0(to_device(lm))
     shape = DecoderShape(g.hidden, g.n_q_heads, g.n_kv_heads, g.head_dim, g.ffn_padded, g.eps,
-                         g.rope_base, L, V, cap, 1)
+                         g.rope_base, L, V, cap, seqs)
     dec = Decoder(shape, layers, to_device(embed), to_device(gamma_f), lm_q, lm_d)
-    for li in range(L):
-        kc, vc = W.kv_prefill_f16(seed, li, g.n_kv_heads, cap, g.head_dim, ctx)
+    for li in range(L if ctx > 0 else 0):
+        kc, vc = W.kv_prefill_f16(seed, li, g.n_kv_heads, cap, g.head_dim, ctx, seqs=seqs)
         dec.k_cache[li].copy_(torch.from_numpy(kc.view(np.int16)))
         dec.v_cache[li].copy_(torch.from_numpy(vc.view(np.int16)))
         if want_host_q4:
@@ -301,6 +302,256 @@ def cpu_decode_baseline(spec, host, first, budget_s: float):
                       f"22-layer workload, oracle in fp64/exact-int C++ with OpenMP"}
 
 
+def graph_time_us(fn, launches: int, rounds: int) -> float:
+    """Average µs per launch of `fn` (which makes `launches` launches),
+    captured once in a graph and replayed `rounds` times; HIP events on the
+    replay stream."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(rounds):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (rounds * launches)
+
+
+def base_line(args, metric, value, unit, ms_per_step, dtype, config):
+    return {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic: seeded N(0,0.02) weights quantized to Q4_0, N(0,1) activations",
+            "config": config}
+
+
+# ---------------------------------------------------------------------------
+# standalone matmul workload: W 5632x2048 and 2048x5632, batch 1 and 8
+# ---------------------------------------------------------------------------
+def run_matmul(args):
+    import numpy as np
+    import torch
+
+    import quantized_q4_q8_amd as qk
+    from quantized_q4_q8_amd.model import to_device
+    from synth import workloads as W
+
+    spec = W.MATMUL
+    rows = []
+    dev = torch.device("cuda")
+    for idx, (n, k) in enumerate(spec["shapes"]):
+        wq, wd = qk.qk_quantize_q4_0(to_device(W.matmul_weight_f32(spec["seed"], idx, n, k)))
+        wbytes = n * k * 9 // 16
+        # distinct copies filling 1 GiB, so that a launch cannot hit the 256 MB
+        # memory-side cache left warm by the previous one
+        copies = -(-(1 << 30) // wbytes)
+        wq_all = wq.unsqueeze(0).repeat(copies, 1, 1)
+        wd_all = wd.unsqueeze(0).repeat(copies, 1, 1)
+        for m in spec["batches"]:
+            xq, xd = qk.quantize_q8_0(to_device(W.matmul_input_f32(spec["seed"], idx, m, k)))
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            nbytes = wbytes + m * k * 34 // 32 + m * n * 4
+            cold = graph_time_us(lambda: [qk.qmatmul_q4_0_q8_0(wq_all[c], wd_all[c], xq, xd, out=y)
+                                          for c in range(copies)], copies, max(2, args.steps))
+            hot = graph_time_us(lambda: [qk.qmatmul_q4_0_q8_0(wq, wd, xq, xd, out=y)
+                                         for _ in range(copies)], copies, max(2, args.steps))
+            rec = {"n": n, "k": k, "m": m, "bytes_per_launch": nbytes,
+                   "cold_us": round(cold, 3), "cold_GBps": round(nbytes / cold / 1e3, 1),
+                   "hot_us": round(hot, 3), "hot_GBps": round(nbytes / hot / 1e3, 1),
+                   "int_ops_per_launch": 2 * m * n * k,
+                   "cold_TOPs": round(2 * m * n * k / cold / 1e6, 3)}
+            log(f"matmul {n}x{k} m={m}: cold {cold:.2f} us {rec['cold_GBps']} GB/s, hot {hot:.2f} us")
+            rows.append(rec)
+        del wq_all, wd_all
+        torch.cuda.empty_cache()
+    head = rows[0]
+    out = base_line(args, "Q4_0 x Q8_0 GEMV GB/s, W 5632x2048 x x[2048], cold memory-side cache",
+                    head["cold_GBps"], "GB/s", head["cold_us"] / 1e3,
+                    "q4_0 x q8_0 (int32 block dots, fp64 accumulate)",
+                    {"workload": "standalone matmul: W 5632x2048 and 2048x5632, batch 1 and 8",
+                     "copies": "1 GiB of distinct weight copies rotated per launch",
+                     "parallelism": "single GPU"})
+    out["roofline"] = {"bound": "hbm", "kernel": "k_gemv (M=1, store epilogue)",
+                       "achieved": head["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(head["cold_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                       "bytes_per_launch": head["bytes_per_launch"], "avg_us": head["cold_us"]}
+    out["shapes"] = rows
+    if not args.no_cpu_baseline:
+        import oracle
+        w = W.matmul_weight_f32(spec["seed"], 0, 5632, 2048)
+        owq, owd = oracle.quantize_q4_0(w)
+        xq, xd = oracle.quantize_q8_0(W.matmul_input_f32(spec["seed"], 0, 1, 2048))
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0) or n == 0:
+            oracle.qmatmul(owq, owd, xq, xd)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        out["cpu_baseline"] = {"value": round(head["bytes_per_launch"] / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{n} oracle GEMVs of W 5632x2048 x x[2048]"}
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# prefill workload: 4 x 512 tokens through the 22-layer model, full logits
+# ---------------------------------------------------------------------------
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import quantized_q4_q8_amd as qk
+    from synth import randint
+    from synth import workloads as W
+
+    spec = W.PREFILL
+    g, L, B, P, V = spec["geometry"], spec["layers"], spec["batch"], spec["prompt"], spec["vocab"]
+    T = B * P
+    want_cpu = not args.no_cpu_baseline
+    dec, _, host = build_decoder(spec, want_cpu, seqs=B)
+    dev = dec.device
+    ids_h = randint(spec["seed"], W.TID_TOKENS, (B, P), V)
+    ids = torch.from_numpy(ids_h.reshape(-1).astype(np.int32)).to(dev)
+    pos = torch.from_numpy(np.tile(np.arange(P, dtype=np.int32), B)).to(dev)
+    seq = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), P)).to(dev)
+    dec.reserve(T)
+    bufs = dec.step_buffers(T)
+    for _ in range(max(1, args.warmup)):
+        dec.step(ids, pos, seq, bufs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dec.step(ids, pos, seq, bufs)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    tok_s = T / (ms / 1e3)
+    H, F, Nqkv = g.hidden, g.ffn_padded, g.n_qkv
+    lin_macs = L * T * H * (Nqkv + g.n_q_heads * g.head_dim + 2 * F) + L * T * F * H + T * V * H
+    log(f"prefill: {ms:.3f} ms per {T}-token step, {tok_s:.0f} tok/s, "
+        f"{2 * lin_macs / (ms / 1e3) / 1e12:.1f} TOP/s over the step")
+
+    # the dominant GEMM alone: gate/up + SwiGLU, M = 2048, N = 2 x 5632, K = 2048
+    xq, xd = qk.quantize_q8_0(torch.randn((T, H), device=dev))
+    h = torch.empty((T, F), dtype=torch.float32, device=dev)
+    rounds = max(2, args.kernel_rounds // 4)
+    us = graph_time_us(lambda: [qk.qk_gate_up_swiglu(lw.w_gate_up_q, lw.w_gate_up_d, xq, xd, out=h)
+                                for lw in dec.layers], L, rounds)
+    ops = 2 * T * 2 * F * H
+    tops = ops / us / 1e6
+    log(f"gate/up GEMM M={T}: {us:.1f} us, {tops:.0f} TOP/s")
+    out = base_line(args, "prefill tokens/s at TinyLLaMA-1.1B Q4_0 shape (4 x 512, full logits)",
+                    tok_s, "tokens/s", ms, "q4_0 x q8_0 int8 MFMA (int32 block dots, fp64 accumulate)",
+                    {"workload": "tinyllama-1.1b-shape causal prefill, batch 4 x 512, 22 layers, full logits",
+                     "tokens_per_step": T, "layers": L, "parallelism": "single GPU"})
+    out["roofline"] = {"bound": "mfma", "kernel": "k_gemm_mfma<EPI_SWIGLU> (gate/up, M=2048)",
+                       "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                       "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                       "ops_per_launch": ops, "avg_us": round(us, 2)}
+    out["step_roofline"] = {"int_ops_per_step": 2 * lin_macs,
+                            "achieved_TOPs": round(2 * lin_macs / (ms / 1e3) / 1e12, 1),
+                            "frac": round(2 * lin_macs / (ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4)}
+    if want_cpu:
+        import oracle
+        cfg = g.cfg(spec["cap"])
+        n = 8
+        kv = [(np.zeros((1, g.n_kv_heads, spec["cap"], g.head_dim), np.uint16),
+               np.zeros((1, g.n_kv_heads, spec["cap"], g.head_dim), np.uint16)) for _ in range(L)]
+        t0 = time.perf_counter()
+        x = oracle.embed_lookup(host["embed"], ids_h[0, :n].astype(np.int32))
+        p = np.arange(n, dtype=np.int32)
+        s0 = np.zeros(n, np.int32)
+        for li in range(L):
+            x = oracle.layer_forward(host["layers"][li], cfg, x, p, s0, kv[li][0], kv[li][1])
+        xq_o, xd_o = oracle.quantize_q8_0(oracle.rmsnorm(x, host["gamma_f"], g.eps))
+        oracle.qmatmul(host["lm_q"], host["lm_d"], xq_o, xd_o)
+        dt = time.perf_counter() - t0
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        out["cpu_baseline"] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"prefill of the first {n} tokens of sequence 0 with full logits"}
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# MoE workload: 256 resident experts, 64 tokens, top-8
+# ---------------------------------------------------------------------------
+def run_moe(args):
+    import numpy as np
+    import torch
+
+    import quantized_q4_q8_amd as qk
+    from quantized_q4_q8_amd.model import to_device
+    from synth import normal
+    from synth import workloads as W
+
+    spec = W.MOE
+    seed, T, H, E, F, k = spec["seed"], spec["tokens"], spec["hidden"], spec["experts"], spec["ffn"], spec["top_k"]
+    dev = torch.device("cuda")
+    t0 = time.time()
+    guq = torch.empty((E, 2 * F, H // 2), dtype=torch.uint8, device=dev)
+    gud = torch.empty((E, 2 * F, H // 32), dtype=torch.int16, device=dev)
+    dnq = torch.empty((E, H, F // 2), dtype=torch.uint8, device=dev)
+    dnd = torch.empty((E, H, F // 32), dtype=torch.int16, device=dev)
+    for e in range(E):
+        gu, dn = W.expert_weights_f32(seed, e, H, F)
+        qk.qk_quantize_q4_0(to_device(gu), out_q=guq[e], out_d=gud[e])
+        qk.qk_quantize_q4_0(to_device(dn), out_q=dnq[e], out_d=dnd[e])
+    torch.cuda.synchronize()
+    log(f"{E} experts resident after {time.time() - t0:.1f}s")
+    x = to_device(normal(seed, W.TID_X, (T, H)))
+    wr = to_device(normal(seed, W.TID_ROUTER, (H, E), W.WEIGHT_STD))
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    sel = torch.empty((T, k), dtype=torch.int32, device=dev)
+    sw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(qk.qk_moe_workspace(T, H, E, k, F), dtype=torch.uint8, device=dev)
+    call = lambda: qk.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd, out=y, sel_idx=sel, sel_w=sw, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    distinct = int(torch.unique(sel).numel())
+    us = graph_time_us(call, 1, max(3, args.steps))
+    per_expert = 3 * F * H * 9 // 16
+    nbytes = distinct * per_expert + H * E * 4 + 2 * T * H * 4
+    gbs = nbytes / us / 1e3
+    log(f"moe: {us:.1f} us per layer, {distinct} distinct experts, {gbs:.0f} GB/s")
+    out = base_line(args, "MoE layer GB/s (256 resident Q4_0 experts, 64 tokens, top-8)", gbs, "GB/s",
+                    us / 1e3, "q4_0 x q8_0 (int32 block dots, fp64 accumulate); fp64 router",
+                    {"workload": "moe layer: hidden 6144, 256 experts x SwiGLU 2048, 64 tokens, top-8",
+                     "distinct_experts": distinct, "parallelism": "single GPU"})
+    out["us_per_layer"] = round(us, 2)
+    out["roofline"] = {"bound": "hbm", "kernel": "whole MoE layer (router, top-k, grouping, grouped GEMVs, combine)",
+                       "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                       "avg_us": round(us, 2)}
+    if not args.no_cpu_baseline:
+        import oracle
+        xs = normal(seed, W.TID_X, (T, H))[:1]
+        wrh = normal(seed, W.TID_ROUTER, (H, E), W.WEIGHT_STD)
+        experts = []
+        sel_o, w_o = oracle.moe_route(xs, wrh, k)
+        for r in range(k):
+            gu, dn = W.expert_weights_f32(seed, int(sel_o[0, r]), H, F)
+            experts.append(oracle.quantize_q4_0(gu) + oracle.quantize_q4_0(dn))
+        t1 = time.perf_counter()
+        sel_o, w_o = oracle.moe_route(xs, wrh, k)
+        acc = np.zeros(H)
+        for r in range(k):
+            acc += w_o[0, r] * oracle.moe_expert_ffn(xs[0], *experts[r])
+        dt = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        out["cpu_baseline"] = {"value": round(8 * per_expert / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle", "sample": "one token through its 8 experts (oracle)"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -314,8 +565,7 @@ def main():
         sys.exit(1)
     import quantized_q4_q8_amd as qk
     qk.load()
-    if args.workload == "decode":
-        run_decode(args)
+    {"decode": run_decode, "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -98,6 +98,28 @@ def test_qmatmul_matches_oracle(gpu_lib, n, k, m):
     assert_same_fp32(host(y), ref)
 
 
+def test_qmatmul_workload_seeded(gpu_lib):
+    """The standalone matmul workload as generated (seed 1): W 5632x2048 and
+    the transposed-shape 2048x5632, at batch 1 and 8, quantized on the GPU."""
+    qk = gpu_lib
+    spec = W.MATMUL
+    for idx, (n, k) in enumerate(spec["shapes"]):
+        w = W.matmul_weight_f32(spec["seed"], idx, n, k)
+        wq, wd = oracle.quantize_q4_0(w)
+        wqg, wdg = qk.qk_quantize_q4_0(dev(w))
+        assert np.array_equal(host(wqg), wq) and np.array_equal(host(wdg, np.uint16), wd)
+        for m in spec["batches"]:
+            say(f"matmul workload n={n} k={k} m={m}")
+            x = W.matmul_input_f32(spec["seed"], idx, m, k)
+            xq, xd = oracle.quantize_q8_0(x)
+            xqg, xdg = qk.quantize_q8_0(dev(x))
+            assert np.array_equal(host(xqg), xq) and np.array_equal(host(xdg, np.uint16), xd)
+            y = qk.qmatmul_q4_0_q8_0(wqg, wdg, xqg, xdg)
+            ref = oracle.qmatmul(wq, wd, xq, xd)
+            assert rel_err(host(y), ref) < LAYER_TOL
+            assert_same_fp32(host(y), ref)
+
+
 @pytest.mark.parametrize("ffn,k,m", [(5632, 2048, 1), (704, 256, 16), (96, 64, 5), (2048, 6144, 3)])
 def test_gate_up_swiglu(gpu_lib, ffn, k, m):
     qk = gpu_lib
