@@ -4,78 +4,67 @@
 // V with a KV cache), TinyLLaMA-in-C++ guide 4.3 (several query heads share
 // one KV head) and 7 (attend over cache rows 0..N).
 //
-// Split over the context: workgroup (chunk c, KV head g, token t) handles
-// cache rows [ACH c, ACH c + ACH) intersected with [0, pos[t]] for all query
-// heads of group g, so each K/V row is read once for the whole group, and
-// writes the chunk's record per head: running max m, exp-sum l and the
-// un-normalized output o.  A second kernel, one workgroup per (head, token),
-// merges the records by log-sum-exp rescaling (every thread issues its loads
-// in one round) and writes the fp32 output and/or its Q8_0 quantization.
-// Cross-workgroup merging inside one kernel would need device-scope release
-// fences, which on this multi-die part write back the whole L2; the kernel
-// boundary is cheaper.  Scores, softmax and the weighted sums are fp64 (K/V
-// rows are widened from fp16 in LDS) and the output is rounded once to fp32.
+// Split over the context in two passes.  The chunk pass reads each 64-row
+// chunk of a KV head once for all query heads of its group and writes one
+// record per (head, chunk); the merge pass combines a head's records by
+// log-sum-exp rescaling.  The kernel boundary between them is the cheapest
+// way to make the records of every die visible to the merging workgroup.
+// Scores, softmax and the weighted sums are fp64 and the output is rounded
+// once to fp32.
 #include "internal.h"
 
 namespace qk {
 
 namespace {
 
-constexpr int MAX_MERGE_CHUNKS = 128;
+constexpr int ACH = 64;            // cache rows per chunk: one per lane
+constexpr int MAX_CHUNKS = 128;    // chunks per head (cap <= 8192)
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int pick_chunk(int64_t tokens, int64_t nkv, int64_t cap) {
-    const int64_t wgs64 = tokens * nkv * ((cap + 63) / 64);
-    return (wgs64 < 512 && (cap + 31) / 32 <= MAX_MERGE_CHUNKS) ? 32 : 64;
-}
-
-}  // namespace
-
-int64_t attention_counter_words(int64_t tokens, int64_t nkv) {
-    (void)tokens;
-    (void)nkv;
-    return 0;
-}
-
-namespace {
-size_t ws_bytes_for(int64_t tokens, int64_t nq, int64_t hd, int64_t nch) {
-    return (size_t)(tokens * nq * nch * (hd + 2)) * sizeof(double);
-}
 }  // namespace
 
 size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t nkv, int64_t hd, int64_t cap) {
-    const int ach = pick_chunk(tokens, nkv, cap);
-    return ws_bytes_for(tokens, nq, hd, (cap + ach - 1) / ach);
+    (void)nkv;
+    const int64_t nch = (cap + ACH - 1) / ACH;
+    return align256((size_t)(tokens * nq * nch * (hd + 2)) * sizeof(double));
 }
 
-template <int HD, int ACH>
-__global__ __launch_bounds__(256) void k_attn_chunk(
+// Chunk pass.  Workgroup (chunk c, KV head g, token t) reads cache rows
+// [64 c, 64 c + 64) intersected with [0, pos[t]] of its sequence once for all
+// query heads of group g; wave w takes query heads w, w + 8, ...  For its head
+// a wave writes the chunk's record: running max m, exp-sum l and the
+// un-normalized output o[hd] (fp64).  Lane = cache row for the scores and the
+// softmax, lane = output dimension for the weighted sum.  q is staged in LDS
+// as fp64, K and V rows as fp32 (exact widenings of fp16), read 128 bits at a
+// time.
+template <int HD>
+__global__ __launch_bounds__(512) void k_attn_chunk(
     const float* __restrict__ q, int64_t q_ts, int64_t nq, int64_t nkv,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, double* __restrict__ part,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, double* __restrict__ rec,
     int64_t nch) {
     constexpr int MAXG = 512 / HD;
-    __shared__ float qs[MAXG][HD];
-    __shared__ __align__(16) float ks[ACH][HD + 1];
+    constexpr int KS = HD + 4;          // K row stride in floats: 16-byte rows, spread over banks
+    constexpr int NW = 8;               // waves per workgroup
+    __shared__ __align__(16) double qs[MAXG][HD];
+    __shared__ __align__(16) float ks[ACH][KS];
     __shared__ __align__(16) float vs[ACH][HD];
-    __shared__ double ps[MAXG][ACH];
+    __shared__ __align__(16) double es[NW][ACH];
 
     const int64_t c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+    const int G = (int)(nq / nkv);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
     const int64_t r0 = c * ACH;
-    if (p < 0 || p >= cap || r0 > p) return;  // out-of-range positions read nothing
+    if (p < 0 || p >= cap || r0 > p) return;   // out-of-range positions read nothing
     const int rows = (int)min((int64_t)ACH, (int64_t)p + 1 - r0);
-    const int G = (int)(nq / nkv);
-    const int tid = threadIdx.x;
     const double rscale = sqrt((double)HD);
 
-    for (int i = tid; i < G * HD; i += 256) {
-        const int hh = i / HD, d = i % HD;
-        qs[hh][d] = q[t * q_ts + (g * G + hh) * HD + d];
-    }
+    for (int i = tid; i < G * HD; i += 512)
+        qs[i / HD][i % HD] = (double)q[t * q_ts + (g * G) * HD + i];
     const int64_t cbase = (((int64_t)seq[t] * nkv + g) * cap + r0) * HD;
-    for (int i = tid; i < ACH * HD / 8; i += 256) {
+    for (int i = tid; i < ACH * HD / 8; i += 512) {
         const int r = (i * 8) / HD, d = (i * 8) % HD;
         uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
         if (r < rows) {
@@ -83,59 +72,72 @@ __global__ __launch_bounds__(256) void k_attn_chunk(
             vv = *reinterpret_cast<const uint4*>(vc + cbase + (int64_t)r * HD + d);
         }
         const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ks[r][d + 2 * e] = h2f((uint16_t)(kw[e] & 0xFFFF));
-            ks[r][d + 2 * e + 1] = h2f((uint16_t)(kw[e] >> 16));
-            vs[r][d + 2 * e] = h2f((uint16_t)(vw[e] & 0xFFFF));
-            vs[r][d + 2 * e + 1] = h2f((uint16_t)(vw[e] >> 16));
-        }
+        float4 k0, k1, v0, v1;
+        k0.x = h2f((uint16_t)(kw[0] & 0xFFFF)); k0.y = h2f((uint16_t)(kw[0] >> 16));
+        k0.z = h2f((uint16_t)(kw[1] & 0xFFFF)); k0.w = h2f((uint16_t)(kw[1] >> 16));
+        k1.x = h2f((uint16_t)(kw[2] & 0xFFFF)); k1.y = h2f((uint16_t)(kw[2] >> 16));
+        k1.z = h2f((uint16_t)(kw[3] & 0xFFFF)); k1.w = h2f((uint16_t)(kw[3] >> 16));
+        v0.x = h2f((uint16_t)(vw[0] & 0xFFFF)); v0.y = h2f((uint16_t)(vw[0] >> 16));
+        v0.z = h2f((uint16_t)(vw[1] & 0xFFFF)); v0.w = h2f((uint16_t)(vw[1] >> 16));
+        v1.x = h2f((uint16_t)(vw[2] & 0xFFFF)); v1.y = h2f((uint16_t)(vw[2] >> 16));
+        v1.z = h2f((uint16_t)(vw[3] & 0xFFFF)); v1.w = h2f((uint16_t)(vw[3] >> 16));
+        *reinterpret_cast<float4*>(&ks[r][d]) = k0;
+        *reinterpret_cast<float4*>(&ks[r][d + 4]) = k1;
+        *reinterpret_cast<float4*>(&vs[r][d]) = v0;
+        *reinterpret_cast<float4*>(&vs[r][d + 4]) = v1;
     }
     __syncthreads();
 
-    for (int i = tid; i < G * ACH; i += 256) {
-        const int hh = i / ACH, r = i % ACH;
+    for (int hh = wave; hh < G; hh += NW) {
+        double* rp = rec + ((t * nq + g * G + hh) * nch + c) * (HD + 2);
         double s = -INFINITY;
-        if (r < rows) {
-            double dot = 0.0;
-#pragma unroll 16
-            for (int d = 0; d < HD; ++d) dot = fma((double)qs[hh][d], (double)ks[r][d], dot);
-            s = dot / rscale;
+        if (lane < rows) {   // score of row `lane`
+            double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+#pragma unroll
+            for (int d = 0; d < HD; d += 4) {
+                const float4 kk = *reinterpret_cast<const float4*>(&ks[lane][d]);
+                const double2 qa = *reinterpret_cast<const double2*>(&qs[hh][d]);
+                const double2 qb = *reinterpret_cast<const double2*>(&qs[hh][d + 2]);
+                d0 = fma(qa.x, (double)kk.x, d0);
+                d1 = fma(qa.y, (double)kk.y, d1);
+                d2 = fma(qb.x, (double)kk.z, d2);
+                d3 = fma(qb.y, (double)kk.w, d3);
+            }
+            s = ((d0 + d1) + (d2 + d3)) / rscale;
         }
-        ps[hh][r] = s;
-    }
-    __syncthreads();
-
-    // softmax pieces of the chunk: one wave per head, lane = row
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int hh = wave; hh < G; hh += 4) {
-        const double s = lane < ACH ? ps[hh][lane] : -INFINITY;
-        const double mx = group_max<WAVE>(s);
-        const double e = lane < rows ? exp(s - mx) : 0.0;
+        const double m = group_max<WAVE>(s);
+        const double e = lane < rows ? exp(s - m) : 0.0;
         const double l = group_sum<WAVE>(e);
-        if (lane < ACH) ps[hh][lane] = e;
-        if (lane == 0) {
-            double* o = part + (((t * nq) + g * G + hh) * nch + c) * (HD + 2);
-            o[0] = mx;
-            o[1] = l;
+        es[wave][lane] = e;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane < HD) {   // weighted values, lane = dimension
+            double o0 = 0.0, o1 = 0.0;
+            int r = 0;
+            for (; r + 1 < rows; r += 2) {
+                const double2 ee = *reinterpret_cast<const double2*>(&es[wave][r]);
+                o0 = fma(ee.x, (double)vs[r][lane], o0);
+                o1 = fma(ee.y, (double)vs[r + 1][lane], o1);
+            }
+            if (r < rows) o0 = fma(es[wave][r], (double)vs[r][lane], o0);
+            rp[2 + lane] = o0 + o1;
         }
+        if (lane == 0) {
+            rp[0] = m;
+            rp[1] = l;
+        }
+        __builtin_amdgcn_wave_barrier();   // es is rewritten for the next head
     }
-    __syncthreads();
-
-    for (int i = tid; i < G * HD; i += 256) {
-        const int hh = i / HD, d = i % HD;
-        double o = 0.0;
-        for (int r = 0; r < rows; ++r) o = fma(ps[hh][r], (double)vs[r][d], o);
-        part[(((t * nq) + g * G + hh) * nch + c) * (HD + 2) + 2 + d] = o;
-    }
-
 }
 
-// Merge the chunk records of head h of token t: M = max m_c, w_c = e^(m_c - M),
-// out = sum_c w_c o_c / sum_c w_c l_c.  256 threads = (HD / 2 output pairs) x
-// (slices of the chunks); slice partial sums are added in LDS in slice order.
-template <int HD, int ACH>
-__global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ part, int64_t nq,
+// Merge pass: workgroup (head h, token t) combines the head's chunk records
+// by log-sum-exp rescaling, out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+// Thread (pair i, slice s) owns output dimensions 2i, 2i + 1 over chunks
+// s, s + SLICES, ...; all of its record loads are issued at once.  Slice sums
+// are added in slice order, so the result does not depend on timing.  Writes
+// the fp32 output and/or its Q8_0 codes (four lanes per block).
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ rec, int64_t nq,
                                                     int64_t nch, int64_t cap,
                                                     const int32_t* __restrict__ pos,
                                                     float* __restrict__ out, int64_t o_ts,
@@ -143,66 +145,77 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ p
                                                     uint16_t* __restrict__ od) {
     constexpr int PAIRS = HD / 2;
     constexpr int SLICES = 256 / PAIRS;
-    constexpr int PER = (MAX_MERGE_CHUNKS + SLICES - 1) / SLICES;
-    __shared__ double w[MAX_MERGE_CHUNKS];
-    __shared__ double red[4];
+    constexpr int PER = (MAX_CHUNKS + SLICES - 1) / SLICES;
+    __shared__ double wsh[MAX_CHUNKS];
+    __shared__ double red[SLICES];
     __shared__ double2 acc_s[SLICES][PAIRS];
     __shared__ double res[HD];
     const int64_t h = blockIdx.x, t = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int p = pos[t];
     const int64_t col = h * HD;
-    if (p < 0 || p >= cap) {   // out-of-range position: zeros, no reads
-        for (int d = tid; d < HD; d += 256) {
-            if (out) out[t * o_ts + col + d] = 0.0f;
-            if (oq) oq[t * o_ts + col + d] = 0;
-        }
-        if (oq && tid < HD / QBLK) od[(t * o_ts + col) / QBLK + tid] = 0;
-        return;
-    }
-    const int64_t used = p / ACH + 1;
-    const double* rec = part + (t * nq + h) * nch * (HD + 2);
-    // chunk weights
-    const double m = tid < used ? rec[tid * (HD + 2)] : -INFINITY;
-    const double l = tid < used ? rec[tid * (HD + 2) + 1] : 0.0;
-    double mx = group_max<WAVE>(m);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    const double wc = tid < used ? exp(m - mx) : 0.0;
-    if (tid < MAX_MERGE_CHUNKS) w[tid] = wc;
-    double ls = group_sum<WAVE>(wc * l);
-    __syncthreads();   // everyone has read red[]
-    if (lane == 0) red[wave] = ls;
-    __syncthreads();
-    const double lsum = (red[0] + red[1]) + (red[2] + red[3]);
-    // weighted outputs: thread (pair, slice) over chunks slice, slice + SLICES, ...
+    const bool valid = p >= 0 && p < cap;   // out-of-range position: zeros, no reads
+    const int used = valid ? p / ACH + 1 : 0;
+    const double* hr = rec + (t * nq + h) * nch * (HD + 2);
     const int pr = tid % PAIRS, sl = tid / PAIRS;
-    double2 xv[PER];
+
+    // every load of this thread at once: its chunks' (m, l) and output pair
+    double2 xv[PER], ml[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int64_t cc = sl + (int64_t)e * SLICES;
-        xv[e] = cc < used ? *reinterpret_cast<const double2*>(rec + cc * (HD + 2) + 2 + 2 * pr)
-                          : make_double2(0.0, 0.0);
+        const int cc = sl + e * SLICES;
+        xv[e] = make_double2(0.0, 0.0);
+        ml[e] = make_double2(-INFINITY, 0.0);
+        if (cc < used) {
+            xv[e] = *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr);
+            if (pr == 0) ml[e] = *reinterpret_cast<const double2*>(hr + cc * (HD + 2));
+        }
     }
+    // M = max over chunks (slice maxima from the pair-0 threads)
+    double mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) mx = fmax(mx, ml[e].x);
+    if (pr == 0) red[sl] = mx;
+    __syncthreads();
+    double M = red[0];
+#pragma unroll
+    for (int q = 1; q < SLICES; ++q) M = fmax(M, red[q]);
+    __syncthreads();   // red is reused below
+    // chunk weights and the slice's share of the normalizer
+    if (pr == 0) {
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int cc = sl + e * SLICES;
+            if (cc < used) {
+                const double w = exp(ml[e].x - M);
+                wsh[cc] = w;
+                ls = fma(w, ml[e].y, ls);
+            }
+        }
+        red[sl] = ls;
+    }
+    __syncthreads();
     double a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int64_t cc = sl + (int64_t)e * SLICES;
-        const double ww = cc < used ? w[cc] : 0.0;
-        a0 = fma(ww, xv[e].x, a0);
-        a1 = fma(ww, xv[e].y, a1);
+        const int cc = sl + e * SLICES;
+        if (cc < used) {
+            a0 = fma(wsh[cc], xv[e].x, a0);
+            a1 = fma(wsh[cc], xv[e].y, a1);
+        }
     }
     acc_s[sl][pr] = make_double2(a0, a1);
     __syncthreads();
     if (tid < PAIRS) {
-        double s0 = 0.0, s1 = 0.0;
+        double lsum = 0.0, s0 = 0.0, s1 = 0.0;
         for (int q = 0; q < SLICES; ++q) {
+            lsum += red[q];
             s0 += acc_s[q][tid].x;
             s1 += acc_s[q][tid].y;
         }
-        res[2 * tid] = s0 / lsum;
-        res[2 * tid + 1] = s1 / lsum;
+        res[2 * tid] = valid ? s0 / lsum : 0.0;
+        res[2 * tid + 1] = valid ? s1 / lsum : 0.0;
     }
     __syncthreads();
     if (tid < HD / 8) {   // four lanes per Q8_0 block
@@ -226,30 +239,27 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ p
 int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
                      int64_t hd, const uint16_t* kc, const uint16_t* vc, int64_t cap,
                      const int32_t* pos, const int32_t* seq, float* out, int64_t o_ts,
-                     int8_t* oq, uint16_t* od, void* ws, size_t ws_bytes, bool counters_zeroed,
-                     hipStream_t s) {
-    (void)counters_zeroed;
+                     int8_t* oq, uint16_t* od, void* ws, size_t ws_bytes, hipStream_t s) {
     if (tokens == 0) return QK_OK;
     if (!ws || ws_bytes < attention_ws_bytes(tokens, nq, nkv, hd, cap)) return QK_EWORKSPACE;
-    const int ach = pick_chunk(tokens, nkv, cap);
-    const int64_t nch = (cap + ach - 1) / ach;
-    if (nch > MAX_MERGE_CHUNKS) return QK_ESHAPE;
-    double* part = static_cast<double*>(ws);
+    const int64_t nch = (cap + ACH - 1) / ACH;
+    if (nch > MAX_CHUNKS || (nq / nkv) * hd > 512) return QK_ESHAPE;
+    double* rec = static_cast<double*>(ws);
     dim3 grid((unsigned)nch, (unsigned)nkv, (unsigned)tokens);
     dim3 mgrid((unsigned)nq, (unsigned)tokens);
-#define QK_ATT(HD_, ACH_)                                                                          \
-    do {                                                                                           \
-        hipLaunchKernelGGL((k_attn_chunk<HD_, ACH_>), grid, dim3(256), 0, s, q, q_ts, nq, nkv, kc, \
-                           vc, cap, pos, seq, part, nch);                                          \
-        hipLaunchKernelGGL((k_attn_merge<HD_, ACH_>), mgrid, dim3(256), 0, s, part, nq, nch, cap,  \
-                           pos, out, o_ts, oq, od);                                                \
-    } while (0)
-    if (hd == 32 && ach == 32) QK_ATT(32, 32);
-    else if (hd == 32) QK_ATT(32, 64);
-    else if (hd == 64 && ach == 32) QK_ATT(64, 32);
-    else if (hd == 64) QK_ATT(64, 64);
-    else return QK_ESHAPE;
-#undef QK_ATT
+    if (hd == 32) {
+        hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
+                           pos, seq, rec, nch);
+        hipLaunchKernelGGL(k_attn_merge<32>, mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
+                           o_ts, oq, od);
+    } else if (hd == 64) {
+        hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
+                           pos, seq, rec, nch);
+        hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
+                           o_ts, oq, od);
+    } else {
+        return QK_ESHAPE;
+    }
     return qk_launch_status();
 }
 
@@ -260,8 +270,7 @@ using namespace qk;
 extern "C" size_t qk_gqa_attention_workspace(int64_t tokens, int64_t n_q_heads, int64_t head_dim,
                                              int64_t cap) {
     if (tokens < 0 || n_q_heads <= 0 || head_dim <= 0 || cap <= 0) return 0;
-    // an upper bound over every KV-head count: records for the 32-row chunk
-    return ws_bytes_for(tokens, n_q_heads, head_dim, (cap + 31) / 32);
+    return attention_ws_bytes(tokens, n_q_heads, n_q_heads, head_dim, cap);
 }
 
 extern "C" int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads,
@@ -273,7 +282,7 @@ extern "C" int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads,
     QK_REQUIRE(n_q_heads % n_kv_heads == 0, QK_ESHAPE);
     QK_REQUIRE(head_dim == 32 || head_dim == 64, QK_ESHAPE);
     QK_REQUIRE((n_q_heads / n_kv_heads) * head_dim <= 512, QK_ESHAPE);
-    QK_REQUIRE(cap <= (int64_t)MAX_MERGE_CHUNKS * 64, QK_ESHAPE);
+    QK_REQUIRE(cap <= (int64_t)MAX_CHUNKS * ACH, QK_ESHAPE);
     if (tokens == 0) return QK_OK;
     QK_REQUIRE(q && k_cache && v_cache && pos && seq && out, QK_EINVAL);
     QK_REQUIRE(QK_ALIGNED(k_cache, 16) && QK_ALIGNED(v_cache, 16) && QK_ALIGNED(q, 4) &&
@@ -283,5 +292,5 @@ extern "C" int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads,
                QK_EWORKSPACE);
     return launch_attention(q, n_q_heads * head_dim, tokens, n_q_heads, n_kv_heads, head_dim,
                             k_cache, v_cache, cap, pos, seq, out, n_q_heads * head_dim, nullptr,
-                            nullptr, ws, ws_bytes, false, (hipStream_t)stream);
+                            nullptr, ws, ws_bytes, (hipStream_t)stream);
 }

@@ -52,6 +52,49 @@ __device__ __forceinline__ T group_max(T v) {
 // result except in vanishingly rare midpoint cases, so the quantization
 // decisions follow the mathematical values and not the summation order.
 
+// -------------------------------------------------------------- RoPE angles
+// sin and cos of a RoPE angle x = position * theta (0 <= x < 2^22) in fp64:
+// Cody-Waite reduction by pi/2 with a two-part constant (the double nearest
+// pi/2 and the double nearest the remainder; fused multiply-adds keep each
+// step to one rounding), the Taylor series of sin and cos on [-pi/4, pi/4]
+// (truncation error below 1e-24), then the quadrant.  Within a few ulps of
+// the correctly rounded values, far below what the fp32 results resolve.
+__device__ __forceinline__ void rope_sincos(double x, double& sn, double& cs) {
+    const double PIO2_HI = 1.5707963267948966;       // nearest double to pi/2
+    const double PIO2_LO = 6.123233995736766e-17;    // nearest double to pi/2 - PIO2_HI
+    const double k = rint(x * 0.6366197723675814);   // x * 2/pi
+    double r = fma(-k, PIO2_HI, x);
+    r = fma(-k, PIO2_LO, r);
+    const double z = r * r;
+    // sin r = r + r^3 (-1/3! + z/5! - z^2/7! + ... + z^9/21!)
+    double p = 1.0 / 51090942171709440000.0;
+    p = fma(p, z, -1.0 / 121645100408832000.0);
+    p = fma(p, z, 1.0 / 355687428096000.0);
+    p = fma(p, z, -1.0 / 1307674368000.0);
+    p = fma(p, z, 1.0 / 6227020800.0);
+    p = fma(p, z, -1.0 / 39916800.0);
+    p = fma(p, z, 1.0 / 362880.0);
+    p = fma(p, z, -1.0 / 5040.0);
+    p = fma(p, z, 1.0 / 120.0);
+    p = fma(p, z, -1.0 / 6.0);
+    const double S = fma(r * z, p, r);
+    // cos r = 1 + z (-1/2! + z/4! - z^2/6! + ... + z^9/20!)
+    double q = 1.0 / 2432902008176640000.0;
+    q = fma(q, z, -1.0 / 6402373705728000.0);
+    q = fma(q, z, 1.0 / 20922789888000.0);
+    q = fma(q, z, -1.0 / 87178291200.0);
+    q = fma(q, z, 1.0 / 479001600.0);
+    q = fma(q, z, -1.0 / 3628800.0);
+    q = fma(q, z, 1.0 / 40320.0);
+    q = fma(q, z, -1.0 / 720.0);
+    q = fma(q, z, 1.0 / 24.0);
+    q = fma(q, z, -0.5);
+    const double C = fma(z, q, 1.0);
+    const int n = (int)((long long)k & 3);
+    sn = n == 0 ? S : (n == 1 ? C : (n == 2 ? -S : -C));
+    cs = n == 0 ? C : (n == 1 ? -S : (n == 2 ? -C : S));
+}
+
 // ------------------------------------------------------------ Q8_0 helpers
 // Four adjacent lanes (lane % 4 == 0..3) hold the 32 values of one block,
 // eight consecutive values each.  Computes d = max|x| / 127 (IEEE division)

@@ -5,16 +5,19 @@
 // y = sum over blocks of delta_w * delta_x * (exact int32 sum of q_w * q_x),
 // with the decode step being a matrix-vector product (same guide, 2.1).
 //
-// Design (CDNA4, wave64): LPR lanes share one weight row, lane i of a row
-// handles blocks i, i + LPR, ...; each lane reads a block's 16 nibble bytes
-// with one 128-bit load (a wave reads 1 KiB of a row contiguously) plus its
-// fp16 scale.  All weight loads of an unrolled step are issued before any
-// arithmetic so each wave keeps ROWS * U 16-byte loads in flight.  Nibbles
-// are unpacked in registers with a mask and a shift; v_dot4_i32_i8 forms the
-// block's integer sum from the unsigned nibbles and the int8 activations, and
-// the -8 offset is applied once per block as -8 * sum(x) (computed per
-// activation block, shared by every row).  Row sums finish with a butterfly
-// over the LPR lanes.  No LDS, no barriers.
+// Design (CDNA4, wave64): a wave owns a few weight rows (one output unit by
+// default) and its 64 lanes split each row: lane i handles blocks i, i + 64,
+// ..., reading a block's 16 nibble bytes with one 128-bit load (a wave reads
+// 1 KiB of a row contiguously) plus its fp16 scale.  All weight loads of a
+// step are issued before anything waits, so every wave has its whole share
+// in flight.  The activation columns are staged once per workgroup in LDS
+// (as Q8_0 codes and fp32 scales, either copied from the input or built by
+// a fused RMSNorm / Q8_0 prologue).  Nibbles are unpacked in registers with a
+// mask and a shift; v_dot4_i32_i8 forms the block's integer sum from the
+// unsigned nibbles and the int8 activations, and the -8 offset is applied
+// once per block as -8 * sum(x).  The wave's row sums are reduced together
+// by a transposed butterfly (tree_sum) and the epilogue runs in the lanes
+// that hold them.
 #include "internal.h"
 
 namespace qk {
@@ -143,24 +146,74 @@ __device__ __forceinline__ void stage_row(const RowRegs<KC>& R, int64_t k, float
     }
 }
 
-template <int M, int LPR, int ROWS, int U, int EPI, int PRO, int KC>
+// Sum of N values per lane over the 64 lanes of a wave, all N at once
+// ("transposed" butterfly): at each of the first log2(N) steps a lane keeps
+// half of its values and adds the partner's copy of them, so N sums cost
+// N - 1 + 6 - log2(N) exchanges instead of 6 N.  Afterwards lane l holds the
+// complete sum of value index tree_index<N>(l); the 64 / N lanes that differ
+// only in their low bits hold the same sum.  The order of additions is fixed,
+// so the result is deterministic.
+template <int N>
+__device__ __forceinline__ double tree_sum(double (&v)[N], int lane) {
+#pragma unroll
+    for (int h = N / 2, o = 32; h >= 1; h >>= 1, o >>= 1) {
+        const bool up = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const double send = up ? v[i] : v[i + h];
+            const double keep = up ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, o, WAVE);
+        }
+    }
+    double s = v[0];
+#pragma unroll
+    for (int o = 32 / N; o >= 1; o >>= 1) s += __shfl_xor(s, o, WAVE);
+    return s;
+}
+
+template <int N>
+__device__ __forceinline__ int tree_index(int lane) {
+    int r = 0;
+#pragma unroll
+    for (int h = N / 2, o = 32; h >= 1; h >>= 1, o >>= 1)
+        if (lane & o) r += h;
+    return r;
+}
+
+// Physical rows per output unit: SwiGLU units are (gate row, up row), QKV
+// units are RoPE pairs (row 2u, row 2u + 1).
+__host__ __device__ constexpr int rows_per_unit(int epi) {
+    return (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2 : 1;
+}
+
+
+// One wave computes R rows (a multiple of the unit size) of the matrix for M
+// activation columns at a time; the four waves of a
+// workgroup take consecutive units.  Each lane reads, per row, blocks lane,
+// lane + 64, ... (U per step) with one 128-bit load each; all loads of a
+// step are issued before the activations are staged, so they are in flight
+// together.  The activations of the workgroup's columns sit in LDS (built
+// there by the prologue, or copied from the Q8_0 input), and are read by
+// every row.
+// KLOOP: K may exceed 64 * U blocks (the weights are then loaded step by
+// step); otherwise the whole row share is loaded at once.
+template <int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
 __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double red[4];
-    constexpr int RL = WAVE / LPR;                                // row groups per wave
-    constexpr int LROWS = (EPI == EPI_SWIGLU) ? ROWS / 2 : ROWS;  // output rows per row group
+    constexpr int RMAX = R;
+    constexpr int P = rows_per_unit(EPI);
+    static_assert(R % P == 0, "rows per wave must hold whole units");
+    constexpr int N = RMAX * M;              // sums per lane in the reduction
+    constexpr int SPAN = WAVE / N;           // lanes holding the same sum
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int lr = lane / LPR;
-    const int li = lane % LPR;
     const int g = blockIdx.y;
+    constexpr int upw = R / P;               // units per wave
 
-    if (a.zero_ptr && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
-
-    const int64_t nlog = (EPI == EPI_SWIGLU) ? a.ffn : a.n;
-    const int64_t wg_base = (int64_t)blockIdx.x * 4 * LROWS * RL;
-    const int64_t lbase = wg_base + (int64_t)wave * LROWS * RL;
+    const int64_t nunits = (EPI == EPI_SWIGLU) ? a.ffn : (EPI == EPI_QKV ? a.n / 2 : a.n);
+    const int64_t wg_unit0 = (int64_t)blockIdx.x * 4 * upw;
+    const int64_t unit0 = wg_unit0 + (int64_t)wave * upw;
 
     int c0 = 0, nc = a.m;
     if (a.col_off) {
@@ -170,24 +223,24 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     if (nc <= 0) return;   // uniform over the workgroup
 
     const int64_t k = a.k, nb = k / QBLK, kh = k / 2;
+    const double* theta = a.rope_theta;   // read in place from the kernel arguments
     const uint8_t* __restrict__ wq = a.wq + (int64_t)g * a.wq_gstride;
     const uint16_t* __restrict__ wd = a.wd + (int64_t)g * a.wd_gstride;
 
-    int64_t orow[ROWS], prow[ROWS];
-    bool rv[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        orow[r] = lbase + lr * LROWS + (r % LROWS);
-        rv[r] = orow[r] < nlog;
-        prow[r] = (EPI == EPI_SWIGLU && r >= LROWS) ? orow[r] + a.ffn : orow[r];
-    }
+    // physical row of register row j (j = unit * P + part)
+    const int64_t ffn = a.ffn;
+    auto prow = [=](int j) -> int64_t {
+        const int64_t unit = unit0 + j / P;
+        const int p = j % P;
+        return (EPI == EPI_SWIGLU) ? unit + p * ffn : (EPI == EPI_QKV ? 2 * unit + p : unit);
+    };
+    auto rvalid = [=](int j) -> bool { return unit0 + j / P < nunits; };
 
-    // LDS: staged activations [M][k] codes, [M][k/32] scales, then the QKV
-    // cos/sin table [M][pairs of this workgroup][2] (fp64)
+    // LDS: activation codes [M][k], scales [M][nb] (fp32), then the argmax
+    // slots [M][4 RMAX]
     int8_t* lxq = reinterpret_cast<int8_t*>(smem);
     float* lxd = reinterpret_cast<float*>(smem + (size_t)M * k);
-    double* lcs = reinterpret_cast<double*>(smem + (((size_t)M * k + (size_t)M * nb * 4 + 7) & ~(size_t)7));
-    constexpr int WG_PAIRS = 4 * LROWS * RL / 2;
+    double* ltail = reinterpret_cast<double*>(smem + (((size_t)M * k + (size_t)M * nb * 4 + 7) & ~(size_t)7));
 
     for (int cc = 0; cc < nc; cc += M) {
         const int mc = nc - cc < M ? nc - cc : M;
@@ -198,186 +251,193 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
             xr[m] = a.col_idx ? a.col_idx[c0 + col] : c0 + col;
         }
 
-        uint4 w[ROWS][U];
-        float dw[ROWS][U];
+        uint4 w[RMAX][U];
+        float dw[RMAX][U];
+        // 32-bit offsets from the (uniform) matrix base: one matrix is below 4 GiB
         auto load_w = [&](int64_t b0) {
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r)
+            for (int j = 0; j < RMAX; ++j) {
+                const uint32_t row = (uint32_t)prow(j);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int64_t b = b0 + u * LPR + li;
-                    if (rv[r] && b < nb) {
-                        w[r][u] = load_stream16(wq + prow[r] * kh + b * 16);
-                        dw[r][u] = h2f(wd[prow[r] * nb + b]);
+                    const uint32_t b = (uint32_t)b0 + u * WAVE + lane;
+                    if (rvalid(j) && b < (uint32_t)nb) {
+                        w[j][u] = load_stream16(wq + (row * (uint32_t)kh + b * 16u));
+                        dw[j][u] = h2f(*reinterpret_cast<const uint16_t*>(
+                            reinterpret_cast<const char*>(wd) + (row * (uint32_t)nb + b) * 2u));
                     } else {
-                        w[r][u] = make_uint4(0, 0, 0, 0);
-                        dw[r][u] = 0.0f;
+                        w[j][u] = make_uint4(0, 0, 0, 0);
+                        dw[j][u] = 0.0f;
                     }
                 }
+            }
         };
 
+        if (cc > 0) lds_barrier();   // the previous pass finished reading LDS
         if (PRO != PRO_NONE) {
-            if (cc > 0) lds_barrier();   // previous chunk finished reading LDS
-            RowRegs<KC> R;
-            load_row<PRO, KC>(R, a.xf + (int64_t)xr[0] * k, a.gamma, k);
+            RowRegs<KC> Rg;
+            load_row<PRO, KC>(Rg, a.xf + (int64_t)xr[0] * k, a.gamma, k);
             load_w(0);                    // weight loads go out behind the row loads
-            stage_row<PRO, KC>(R, k, a.eps, red, lxq, lxd);
+            stage_row<PRO, KC>(Rg, k, a.eps, red, lxq, lxd);
 #pragma unroll
             for (int m = 1; m < M; ++m) {
                 if (m >= mc) break;       // uniform over the workgroup
                 lds_barrier();            // `red` reused
-                load_row<PRO, KC>(R, a.xf + (int64_t)xr[m] * k, a.gamma, k);
-                stage_row<PRO, KC>(R, k, a.eps, red, lxq + (size_t)m * k, lxd + (size_t)m * nb);
+                load_row<PRO, KC>(Rg, a.xf + (int64_t)xr[m] * k, a.gamma, k);
+                stage_row<PRO, KC>(Rg, k, a.eps, red, lxq + (size_t)m * k, lxd + (size_t)m * nb);
             }
-            if (EPI == EPI_QKV) {
-                // cos/sin of this workgroup's q/k row pairs, per column, in fp64
-                for (int i = threadIdx.x; i < mc * WG_PAIRS; i += 256) {
-                    const int m = i / WG_PAIRS, pr = i % WG_PAIRS;
-                    const int64_t row = wg_base + 2 * pr;
-                    double cs = 1.0, sn = 0.0;
-                    if (row < a.q_rows + a.kv_rows) {
-                        const int64_t pair = (row % a.hd) / 2;
-                        const double theta = pow((double)a.rope_base, -2.0 * (double)pair / (double)a.hd);
-                        sincos((double)a.pos[c0 + cc + m] * theta, &sn, &cs);
-                    }
-                    lcs[2 * i] = cs;
-                    lcs[2 * i + 1] = sn;
+        } else {
+            // copy the Q8_0 columns into LDS: the first XREG chunks per thread
+            // are loaded before the weights, the rest after
+            constexpr int XREG = M >= 4 ? 2 : 1;
+            const int64_t c16 = k / 16, tot = (int64_t)mc * c16, totd = (int64_t)mc * nb;
+            // activation row of pass column m (m < mc), looked up per use
+            const int32_t* __restrict__ cidx = a.col_idx;
+            auto col_row = [=](int m) -> int64_t {
+                const int col = c0 + cc + m;
+                return cidx ? (int64_t)cidx[col] : (int64_t)col;
+            };
+            uint4 xs[XREG];
+            float xds;
+#pragma unroll
+            for (int p = 0; p < XREG; ++p) {
+                const int64_t i = threadIdx.x + (int64_t)p * 256;
+                xs[p] = make_uint4(0, 0, 0, 0);
+                if (i < tot) {
+                    const int64_t r = col_row((int)(i / c16));
+                    xs[p] = *reinterpret_cast<const uint4*>(a.xq + r * k + (i % c16) * 16);
                 }
             }
-            lds_barrier();
-        } else {
+            xds = 0.0f;
+            if (threadIdx.x < totd) xds = h2f(a.xd[col_row((int)(threadIdx.x / nb)) * nb + threadIdx.x % nb]);
             load_w(0);
+#pragma unroll
+            for (int p = 0; p < XREG; ++p) {
+                const int64_t i = threadIdx.x + (int64_t)p * 256;
+                if (i < tot) *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) = xs[p];
+            }
+            for (int64_t i = threadIdx.x + (int64_t)XREG * 256; i < tot; i += 256)
+                *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) =
+                    *reinterpret_cast<const uint4*>(a.xq + col_row((int)(i / c16)) * k + (i % c16) * 16);
+            if (threadIdx.x < totd) lxd[threadIdx.x] = xds;
+            for (int64_t i = threadIdx.x + 256; i < totd; i += 256)
+                lxd[i] = h2f(a.xd[col_row((int)(i / nb)) * nb + i % nb]);
         }
+        lds_barrier();
 
-        double acc[ROWS][M];
+        double acc[RMAX][M];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r)
+        for (int j = 0; j < RMAX; ++j)
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = 0.0;
+            for (int m = 0; m < M; ++m) acc[j][m] = 0.0;
 
-        for (int64_t b0 = 0; b0 < nb; b0 += (int64_t)LPR * U) {
-            if (b0 > 0) load_w(b0);
+        for (int64_t b0 = 0; b0 < nb; b0 += (int64_t)WAVE * U) {
+            if (KLOOP && b0 > 0) load_w(b0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t b = b0 + u * LPR + li;
+                const int64_t b = b0 + u * WAVE + lane;
                 if (b >= nb) break;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    uint4 x0, x1;
-                    float dx;
-                    if (PRO != PRO_NONE) {
-                        const int8_t* xp = lxq + (size_t)m * k + b * QBLK;
-                        x0 = *reinterpret_cast<const uint4*>(xp);
-                        x1 = *reinterpret_cast<const uint4*>(xp + 16);
-                        dx = lxd[(size_t)m * nb + b];
-                    } else {
-                        const int8_t* xp = a.xq + (int64_t)xr[m] * k + b * QBLK;
-                        x0 = *reinterpret_cast<const uint4*>(xp);
-                        x1 = *reinterpret_cast<const uint4*>(xp + 16);
-                        dx = h2f(a.xd[(int64_t)xr[m] * nb + b]);
-                    }
+                    const int8_t* xp = lxq + (size_t)m * k + b * QBLK;
+                    const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+                    const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 16);
+                    const float dx = lxd[(size_t)m * nb + b];
                     const int s0 = -8 * byte_sum(x0, x1);
 #pragma unroll
-                    for (int r = 0; r < ROWS; ++r) {
+                    for (int j = 0; j < RMAX; ++j) {
                         // dw * dx is exact in fp32 (two fp16 values); times the
                         // int32 block dot it is exact in fp64
-                        const int s = dot_block(w[r][u], x0, x1, s0);
-                        acc[r][m] = fma((double)(dw[r][u] * dx), (double)s, acc[r][m]);
+                        const int sdot = dot_block(w[j][u], x0, x1, s0);
+                        acc[j][m] = fma((double)(dw[j][u] * dx), (double)sdot, acc[j][m]);
                     }
                 }
             }
+            if (!KLOOP) break;
         }
 
+        // all row/column sums of the wave at once; value index r = m * RMAX + j
+        double v[N];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = group_sum<LPR>(acc[r][m]);
+            for (int j = 0; j < RMAX; ++j) v[m * RMAX + j] = acc[j][m];
+        const double s = tree_sum<N>(v, lane);
+        const int r = tree_index<N>(lane);
+        const int m = r / RMAX, j = r % RMAX;
+        const bool owner = (lane & (SPAN - 1)) == 0 && rvalid(j) && cc + m < nc;
+        const int64_t row = prow(j);
+        const int64_t ocol = c0 + cc + m;
 
-        if (EPI == EPI_ARGMAX) {
-            // logits, then the workgroup's best (value, lowest row) per column
-            float* bv = reinterpret_cast<float*>(lcs);          // [4 * RL][M], after the staged x
-            int* bi = reinterpret_cast<int*>(bv + 4 * RL * M);
-            if (li == 0) {
-                const int slot = wave * RL + lr;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float best = -INFINITY;
-                    int besti = INT32_MAX;
-#pragma unroll
-                    for (int r = 0; r < ROWS; ++r) {
-                        if (!rv[r] || cc + m >= nc) continue;
-                        const float v = (float)acc[r][m];
-                        a.y[(int64_t)(c0 + cc + m) * a.ldy + prow[r]] = v;
-                        if (v > best || (v == best && (int)prow[r] < besti)) {
-                            best = v;
-                            besti = (int)prow[r];
-                        }
+        if (EPI == EPI_STORE) {
+            if (owner) {
+                float o = (float)s;
+                if (a.residual) o = a.residual[ocol * a.ldr + row] + o;
+                a.y[ocol * a.ldy + row] = o;
+            }
+        } else if (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+            // the unit's second row sits in the lane whose index differs in
+            // the bit that the last halving step decided
+            const double s2 = __shfl_xor(s, WAVE / N, WAVE);
+            if (owner && (j % 2) == 0) {
+                const int64_t unit = unit0 + j / 2;
+                if (EPI == EPI_SWIGLU) {
+                    a.y[ocol * a.ldy + unit] = swiglu1((float)s, (float)s2);
+                } else {
+                    // RoPE angle of this pair in fp64, computed here where the
+                    // weight registers are free
+                    const int64_t row0 = 2 * unit;
+                    const int p = a.pos[ocol];
+                    double c = 1.0, sn = 0.0;
+                    if (row0 < a.q_rows + a.kv_rows)
+                        rope_sincos((double)p * theta[(row0 % a.hd) / 2], sn, c);
+                    const double x1 = (double)(float)s, x2 = (double)(float)s2;
+                    if (row0 < a.q_rows) {
+                        a.q_out[ocol * a.q_rows + row0] = (float)(x1 * c - x2 * sn);
+                        a.q_out[ocol * a.q_rows + row0 + 1] = (float)(x1 * sn + x2 * c);
+                    } else if (p >= 0 && p < a.cap) {
+                        const bool is_k = row0 < a.q_rows + a.kv_rows;
+                        const int64_t rr = row0 - a.q_rows - (is_k ? 0 : a.kv_rows);
+                        const int64_t gh = rr / a.hd, d = rr % a.hd;
+                        const int64_t dst = (((int64_t)a.seq[ocol] * a.n_kv + gh) * a.cap + p) * a.hd + d;
+                        uint16_t* cache = is_k ? a.kc : a.vc;
+                        const float o1 = (float)(is_k ? x1 * c - x2 * sn : x1);
+                        const float o2 = (float)(is_k ? x1 * sn + x2 * c : x2);
+                        cache[dst] = f2h(o1);
+                        cache[dst + 1] = f2h(o2);
                     }
-                    bv[slot * M + m] = best;
-                    bi[slot * M + m] = besti;
                 }
             }
+        } else {  // EPI_ARGMAX: logits, then the workgroup's best (value, lowest row) per column
+            constexpr int SLOTS = 4 * RMAX;
+            float* bv = reinterpret_cast<float*>(ltail);
+            int* bi = reinterpret_cast<int*>(bv + M * SLOTS);
+            for (int i = threadIdx.x; i < M * SLOTS; i += 256) {
+                bv[i] = -INFINITY;
+                bi[i] = INT32_MAX;
+            }
             lds_barrier();
-            if (threadIdx.x < M && (int)threadIdx.x < mc) {
-                const int m = threadIdx.x;
+            if (owner) {
+                const float o = (float)s;
+                a.y[ocol * a.ldy + row] = o;
+                bv[m * SLOTS + wave * RMAX + j] = o;
+                bi[m * SLOTS + wave * RMAX + j] = (int)row;
+            }
+            lds_barrier();
+            if ((int)threadIdx.x < mc) {
+                const int mm = threadIdx.x;
                 float best = -INFINITY;
                 int besti = INT32_MAX;
-                for (int sl = 0; sl < 4 * RL; ++sl) {
-                    const float v = bv[sl * M + m];
-                    const int i = bi[sl * M + m];
-                    if (v > best || (v == best && i < besti)) {
-                        best = v;
+                for (int sl = 0; sl < SLOTS; ++sl) {
+                    const float o = bv[mm * SLOTS + sl];
+                    const int i = bi[mm * SLOTS + sl];
+                    if (o > best || (o == best && i < besti)) {
+                        best = o;
                         besti = i;
                     }
                 }
-                a.part_val[(int64_t)(cc + m) * gridDim.x + blockIdx.x] = best;
-                a.part_idx[(int64_t)(cc + m) * gridDim.x + blockIdx.x] = besti;
-            }
-            lds_barrier();
-        } else if (li == 0) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                if (cc + m >= nc) break;
-                const int64_t ocol = c0 + cc + m;
-                if (EPI == EPI_STORE) {
-#pragma unroll
-                    for (int r = 0; r < ROWS; ++r) {
-                        if (!rv[r]) continue;
-                        float v = (float)acc[r][m];
-                        if (a.residual) v = a.residual[ocol * a.ldr + prow[r]] + v;
-                        a.y[ocol * a.ldy + prow[r]] = v;
-                    }
-                } else if (EPI == EPI_SWIGLU) {
-#pragma unroll
-                    for (int r = 0; r < LROWS; ++r) {
-                        if (!rv[r]) continue;
-                        a.y[ocol * a.ldy + orow[r]] = swiglu1((float)acc[r][m], (float)acc[r + LROWS][m]);
-                    }
-                } else {  // EPI_QKV: rows orow[r], orow[r] + 1 form one RoPE pair
-#pragma unroll
-                    for (int r = 0; r < ROWS; r += 2) {
-                        if (!rv[r]) continue;
-                        const int64_t row = orow[r];
-                        const int pr = (int)((row - wg_base) / 2);
-                        const double c = lcs[2 * (m * WG_PAIRS + pr)], sn = lcs[2 * (m * WG_PAIRS + pr) + 1];
-                        const double x1 = (double)(float)acc[r][m], x2 = (double)(float)acc[r + 1][m];
-                        const int p = a.pos[ocol];
-                        if (row < a.q_rows) {
-                            a.q_out[ocol * a.q_rows + row] = (float)(x1 * c - x2 * sn);
-                            a.q_out[ocol * a.q_rows + row + 1] = (float)(x1 * sn + x2 * c);
-                        } else if (p >= 0 && p < a.cap) {
-                            const bool is_k = row < a.q_rows + a.kv_rows;
-                            const int64_t rr = row - a.q_rows - (is_k ? 0 : a.kv_rows);
-                            const int64_t gh = rr / a.hd, d = rr % a.hd;
-                            const int64_t dst = (((int64_t)a.seq[ocol] * a.n_kv + gh) * a.cap + p) * a.hd + d;
-                            uint16_t* cache = is_k ? a.kc : a.vc;
-                            const float o1 = (float)(is_k ? x1 * c - x2 * sn : x1);
-                            const float o2 = (float)(is_k ? x1 * sn + x2 * c : x2);
-                            cache[dst] = f2h(o1);
-                            cache[dst + 1] = f2h(o2);
-                        }
-                    }
-                }
+                a.part_val[(int64_t)(cc + mm) * gridDim.x + blockIdx.x] = best;
+                a.part_idx[(int64_t)(cc + mm) * gridDim.x + blockIdx.x] = besti;
             }
         }
     }
@@ -422,113 +482,129 @@ int launch_argmax_partials(const float* part_val, const int32_t* part_idx, int64
 
 namespace {
 
-int pick_m(int64_t max_cols) { return max_cols <= 1 ? 1 : (max_cols <= 4 ? 4 : 8); }
-int pick_lpr(int64_t k) { return k / QBLK >= 48 ? 64 : 16; }
+int pick_m(int64_t cols) { return cols <= 1 ? 1 : (cols <= 2 ? 2 : (cols <= 4 ? 4 : 8)); }
 
-// Rows per row group: four for tall matrices, two otherwise (and always two
-// for the RoPE pairs of EPI_QKV), so that small matrices still spread over all
-// 256 CUs.
-int pick_rows(int epi, int64_t nlog, int lpr) {
-    const int64_t rl = WAVE / lpr;
-    if (epi == EPI_QKV) return 2;
-    if (epi == EPI_SWIGLU) return nlog / rl >= 4096 ? 4 : 2;
-    return nlog / rl >= 8192 ? 4 : 2;
+size_t stage_bytes(int M, int64_t k) {
+    return (((size_t)M * k + (size_t)M * (k / QBLK) * 4) + 7) & ~(size_t)7;
 }
 
-size_t lds_bytes(int pro, int epi, int M, int64_t k, int lpr, int rows) {
-    const int rl = WAVE / lpr;
-    const int lrows = epi == EPI_SWIGLU ? rows / 2 : rows;
-    size_t b = 0;
-    if (pro != PRO_NONE) b = (size_t)M * k + (size_t)M * (k / QBLK) * 4;
-    b = (b + 7) & ~(size_t)7;
-    if (epi == EPI_QKV) b += (size_t)M * (4 * lrows * rl / 2) * 16;
-    if (epi == EPI_ARGMAX) b += (size_t)4 * rl * M * 8;
+// Physical rows per wave.  Kernels that stage their activations with a
+// fused RMSNorm prologue run two units per wave (fewer workgroups repeat the
+// prologue); the others one unit per wave until the launch has more than
+// 8192 units, then two, then four (two at most for 4 or 8 columns per pass).
+// Small per-wave work and many waves keep the most loads in flight per CU.
+int pick_rows(int epi, int pro, int M, int64_t units) {
+    const int P = rows_per_unit(epi);
+    const int cap = M <= 2 ? 4 : 2;
+    int upw = units > 2 * 8192 ? 4 : (units > 8192 ? 2 : 1);
+    if (pro == PRO_RMSNORM && epi == EPI_SWIGLU && units >= 2048) upw = std::max(upw, 2);
+    while (upw * P > cap) upw /= 2;
+    return std::max(1, upw) * P;
+}
+
+size_t lds_bytes(int epi, int M, int64_t k, int rows) {
+    size_t b = stage_bytes(M, k);
+    if (epi == EPI_ARGMAX) b += (size_t)M * 4 * rows * 8;
     return b;
 }
 
-// Blocks per lane loaded together: enough to cover a row in one step for the
-// common K (one for K <= 32 * LPR, three for K <= 96 * LPR at M = 1), fewer
-// for wide M where the activations take the registers.
-int pick_u(int M, int64_t k, int lpr) {
-    const int64_t need = (k / QBLK + lpr - 1) / lpr;
-    if (M == 1) return need <= 1 ? 1 : 3;
-    if (M == 4) return need <= 1 ? 1 : 2;
-    return 1;
+constexpr size_t LDS_LIMIT = 64 * 1024;
+
+int64_t units_of(const GemvArgs& a, int epi) {
+    return epi == EPI_SWIGLU ? a.ffn : (epi == EPI_QKV ? a.n / 2 : a.n);
 }
 
-template <int M, int LPR, int ROWS, int EPI, int PRO, int U, int KC>
+// columns per pass: what the groups need on average, capped by LDS
+int pick_cols(const GemvArgs& a, int epi) {
+    int M = pick_m(a.max_cols);
+    while (M > 1 && lds_bytes(epi, M, a.k, 4) > LDS_LIMIT) M /= 2;
+    return M;
+}
+
+template <int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
 void launch_cfg(const GemvArgs& a, hipStream_t s) {
-    constexpr int RL = WAVE / LPR;
-    constexpr int LROWS = (EPI == EPI_SWIGLU) ? ROWS / 2 : ROWS;
-    const int64_t nlog = (EPI == EPI_SWIGLU) ? a.ffn : a.n;
-    const int64_t per_wg = 4 * (int64_t)LROWS * RL;
-    dim3 grid((unsigned)((nlog + per_wg - 1) / per_wg), (unsigned)a.groups);
-    const size_t lds = lds_bytes(PRO, EPI, M, a.k, LPR, ROWS);
-    hipLaunchKernelGGL((k_gemv<M, LPR, ROWS, U, EPI, PRO, KC>), grid, dim3(256), lds, s, a);
+    const int64_t units = units_of(a, EPI);
+    const int64_t per_wg = 4 * (int64_t)(R / rows_per_unit(EPI));
+    dim3 grid((unsigned)((units + per_wg - 1) / per_wg), (unsigned)a.groups);
+    hipLaunchKernelGGL((k_gemv<M, R, U, EPI, PRO, KC, KLOOP>), grid, dim3(256),
+                       lds_bytes(EPI, M, a.k, R), s, a);
 }
 
-template <int M, int LPR, int EPI, int PRO, int U, int KC>
-void launch_rows_kc(const GemvArgs& a, hipStream_t s) {
-    const int64_t nlog = (EPI == EPI_SWIGLU) ? a.ffn : a.n;
-    if constexpr (EPI == EPI_QKV) {
-        launch_cfg<M, LPR, 2, EPI, PRO, U, KC>(a, s);
-    } else {
-        if (pick_rows(EPI, nlog, LPR) == 4) launch_cfg<M, LPR, 4, EPI, PRO, U, KC>(a, s);
-        else launch_cfg<M, LPR, 2, EPI, PRO, U, KC>(a, s);
+template <int M, int U, int EPI, int PRO, int KC, bool KLOOP>
+void launch_r(const GemvArgs& a, hipStream_t s) {
+    constexpr int P = rows_per_unit(EPI);
+    const int R = pick_rows(EPI, PRO, M, units_of(a, EPI) * a.groups);
+    if constexpr (M <= 2) {
+        if (R >= 4) { launch_cfg<M, 4, U, EPI, PRO, KC, KLOOP>(a, s); return; }
     }
+    if constexpr (P == 1) {
+        if (R == 1) { launch_cfg<M, 1, U, EPI, PRO, KC, KLOOP>(a, s); return; }
+    }
+    launch_cfg<M, 2, U, EPI, PRO, KC, KLOOP>(a, s);
 }
 
 // Prologue chunks (2048 values each) held in registers: one for K <= 2048.
-template <int M, int LPR, int EPI, int PRO, int U>
-void launch_rows(const GemvArgs& a, hipStream_t s) {
+template <int M, int U, int EPI, int PRO, bool KLOOP>
+void launch_kc(const GemvArgs& a, hipStream_t s) {
     if constexpr (PRO == PRO_NONE) {
-        launch_rows_kc<M, LPR, EPI, PRO, U, 1>(a, s);
+        launch_r<M, U, EPI, PRO, 1, KLOOP>(a, s);
     } else {
-        if (a.k <= 2048) launch_rows_kc<M, LPR, EPI, PRO, U, 1>(a, s);
-        else launch_rows_kc<M, LPR, EPI, PRO, U, PRO_CHUNKS>(a, s);
+        if (a.k <= 2048) launch_r<M, U, EPI, PRO, 1, KLOOP>(a, s);
+        else launch_r<M, U, EPI, PRO, PRO_CHUNKS, KLOOP>(a, s);
     }
 }
 
-template <int M, int LPR, int EPI, int PRO>
-void launch_u(const GemvArgs& a, hipStream_t s) {
-    constexpr int UHI = M == 1 ? 3 : (M == 4 ? 2 : 1);
-    if (pick_u(M, a.k, LPR) == 1) launch_rows<M, LPR, EPI, PRO, 1>(a, s);
-    else launch_rows<M, LPR, EPI, PRO, UHI>(a, s);
-}
-
+// Blocks per lane per step: one for K <= 2048, three up to K = 6144 (one
+// step either way); longer rows (no prologue) loop over steps of three.
 template <int M, int EPI, int PRO>
-void launch_lpr(const GemvArgs& a, hipStream_t s) {
-    if (pick_lpr(a.k) == 64) launch_u<M, 64, EPI, PRO>(a, s);
-    else launch_u<M, 16, EPI, PRO>(a, s);
+void launch_u(const GemvArgs& a, hipStream_t s) {
+    const int64_t nb = a.k / QBLK;
+    if (nb <= WAVE) {
+        launch_kc<M, 1, EPI, PRO, false>(a, s);
+    } else if (nb <= 3 * WAVE) {
+        launch_kc<M, 3, EPI, PRO, false>(a, s);
+    } else {
+        if constexpr (PRO == PRO_NONE && (EPI == EPI_STORE || EPI == EPI_SWIGLU))
+            launch_kc<M, 3, EPI, PRO, true>(a, s);
+    }
 }
 
 template <int EPI, int PRO>
 void launch_m(const GemvArgs& a, hipStream_t s) {
-    switch (pick_m(a.max_cols)) {
-        case 1: launch_lpr<1, EPI, PRO>(a, s); break;
-        case 4: launch_lpr<4, EPI, PRO>(a, s); break;
-        default: launch_lpr<8, EPI, PRO>(a, s); break;
+    switch (pick_cols(a, EPI)) {
+        case 1: launch_u<1, EPI, PRO>(a, s); break;
+        case 2: launch_u<2, EPI, PRO>(a, s); break;
+        case 4: launch_u<4, EPI, PRO>(a, s); break;
+        default: launch_u<8, EPI, PRO>(a, s); break;
     }
 }
 
 }  // namespace
 
+bool gemv_fits(int64_t k) { return lds_bytes(EPI_ARGMAX, 1, k, 2) <= LDS_LIMIT; }
+
 bool gemv_prologue_fits(int64_t k, int64_t max_cols) {
-    const int M = pick_m(max_cols);
-    return k <= (int64_t)PRO_CHUNKS * 2048 &&
-           lds_bytes(PRO_RMSNORM, EPI_QKV, M, k, pick_lpr(k), 2) <= 60 * 1024;
+    (void)max_cols;
+    return k <= (int64_t)PRO_CHUNKS * 2048 && gemv_fits(k);
 }
 
 int64_t gemv_argmax_parts(int64_t n, int64_t k, int64_t max_cols) {
-    (void)max_cols;
-    const int lpr = pick_lpr(k);
-    const int rows = pick_rows(EPI_ARGMAX, n, lpr);
-    const int64_t per_wg = 4 * (int64_t)rows * (WAVE / lpr);
+    GemvArgs a{};
+    a.n = n; a.k = k; a.max_cols = (int32_t)max_cols; a.groups = 1;
+    const int M = pick_cols(a, EPI_ARGMAX);
+    const int R = pick_rows(EPI_ARGMAX, PRO_RMSNORM, M, n);
+    const int64_t per_wg = 4 * (int64_t)(M <= 2 ? R : std::min(R, 2));
     return (n + per_wg - 1) / per_wg;
 }
 
 int launch_gemv(const GemvArgs& a, int epi, hipStream_t s, int pro) {
+    if (!gemv_fits(a.k)) return QK_ESHAPE;
+    // one matrix below 4 GiB of nibbles (32-bit offsets in the kernel)
+    if ((uint64_t)a.n * (uint64_t)(a.k / 2) >= (1ull << 32)) return QK_ESHAPE;
+    if (a.k / QBLK > 3 * WAVE && (pro != PRO_NONE || (epi != EPI_STORE && epi != EPI_SWIGLU)))
+        return QK_ESHAPE;
     if (pro != PRO_NONE && !gemv_prologue_fits(a.k, a.max_cols)) return QK_ESHAPE;
+    if (epi == EPI_QKV && (a.hd % 2 || a.q_rows % 2 || a.kv_rows % 2)) return QK_ESHAPE;
     if (epi == EPI_SWIGLU) {
         if (pro == PRO_RMSNORM) launch_m<EPI_SWIGLU, PRO_RMSNORM>(a, s);
         else launch_m<EPI_SWIGLU, PRO_NONE>(a, s);
@@ -563,7 +639,7 @@ extern "C" int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_
     a.xq = x_q; a.xd = x_d; a.m = (int32_t)m; a.groups = 1;
     a.y = y; a.ldy = n; a.residual = nullptr; a.ldr = 0; a.ffn = 0;
     a.max_cols = (int32_t)m;
-    if (m > 8) return launch_gemm(a, EPI_STORE, (hipStream_t)stream);
+    if (m > 8 || !gemv_fits(k)) return launch_gemm(a, EPI_STORE, (hipStream_t)stream);
     return launch_gemv(a, EPI_STORE, (hipStream_t)stream);
 }
 
@@ -583,6 +659,6 @@ extern "C" int qk_gate_up_swiglu(const uint8_t* w_q, const uint16_t* w_d, int64_
     a.xq = x_q; a.xd = x_d; a.m = (int32_t)m; a.groups = 1;
     a.y = h; a.ldy = ffn; a.residual = nullptr; a.ldr = 0; a.ffn = ffn;
     a.max_cols = (int32_t)m;
-    if (m > 8) return launch_gemm(a, EPI_SWIGLU, (hipStream_t)stream);
+    if (m > 8 || !gemv_fits(k)) return launch_gemm(a, EPI_SWIGLU, (hipStream_t)stream);
     return launch_gemv(a, EPI_SWIGLU, (hipStream_t)stream);
 }

@@ -40,7 +40,7 @@ struct GemvArgs {
     const float* residual;
     int64_t ldr;
     int64_t ffn;             // EPI_SWIGLU: gate rows [0, ffn), up rows [ffn, 2 ffn)
-    int32_t max_cols;        // upper bound of columns per group (picks the tile)
+    int32_t max_cols;        // typical columns per group (picks columns per pass)
     // prologue (PRO_RMSNORM / PRO_Q8): fp32 activations [rows][k], gain, eps
     const float* xf;
     const float* gamma;
@@ -49,6 +49,7 @@ struct GemvArgs {
     // head_dim hd, n_kv heads, caches [seqs][n_kv][cap][hd]; q_out [m][q_rows]
     int64_t q_rows, kv_rows, hd, n_kv, cap;
     float rope_base;
+    double rope_theta[64];   // theta_i = rope_base^(-2i/hd) for i < hd/2 (hd <= 128), set by the host
     const int32_t* pos;
     const int32_t* seq;
     uint16_t* kc;
@@ -57,15 +58,14 @@ struct GemvArgs {
     // EPI_ARGMAX: partials [column][workgroup]
     float* part_val;
     int32_t* part_idx;
-    // workgroup (0, 0) zeroes zero_n words at zero_ptr (counters of a later kernel)
-    int32_t* zero_ptr;
-    int32_t zero_n;
 };
 
 // Launch the GEMV with the given epilogue and prologue; returns QK_ESHAPE when
 // the prologue's LDS staging would not fit (the caller then stages itself).
 int launch_gemv(const GemvArgs& a, int epi, hipStream_t s, int pro = PRO_NONE);
 bool gemv_prologue_fits(int64_t k, int64_t max_cols);
+// Whether one activation column of length k fits the GEMV's LDS staging.
+bool gemv_fits(int64_t k);
 
 // Final step of EPI_ARGMAX: idx[c] = index of the best partial of column c.
 int launch_argmax_partials(const float* part_val, const int32_t* part_idx, int64_t nparts,
@@ -95,13 +95,11 @@ int launch_rope_kv(float* base, int64_t tokens, int64_t tok_stride, int64_t q_of
 // Attention with explicit q/out token strides (elements): a chunk kernel and a
 // merge kernel.  The merge writes fp32 `out` (when non-null) and/or the Q8_0
 // of the output row (oq, od; when non-null, with out_tok_stride also the Q8_0
-// row length).  `counters_zeroed` is unused (no counters).
+// row length).
 int launch_attention(const float* q, int64_t q_tok_stride, int64_t tokens, int64_t nq,
                      int64_t nkv, int64_t hd, const uint16_t* kc, const uint16_t* vc, int64_t cap,
                      const int32_t* pos, const int32_t* seq, float* out, int64_t out_tok_stride,
-                     int8_t* oq, uint16_t* od, void* ws, size_t ws_bytes, bool counters_zeroed,
-                     hipStream_t s);
+                     int8_t* oq, uint16_t* od, void* ws, size_t ws_bytes, hipStream_t s);
 size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t nkv, int64_t hd, int64_t cap);
-int64_t attention_counter_words(int64_t tokens, int64_t nkv);
 
 }  // namespace qk

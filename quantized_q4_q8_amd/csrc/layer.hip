@@ -6,6 +6,8 @@
 // SwiGLU feed-forward half, which repeats the norm -> projection -> residual
 // pattern with its own gain.  Every Q4_0 matmul reads Q8_0 activations
 // (llama.cpp guide 2.2); the FFN input is quantized once for gate and up.
+#include <cmath>
+
 #include "internal.h"
 
 namespace qk {
@@ -91,9 +93,11 @@ int layer_decode(const qk_layer* w, const qk_layer_cfg& c, float* x, int64_t T,
     a.xf = x; a.gamma = w->gamma_attn; a.eps = c.eps;
     a.q_rows = Nq; a.kv_rows = Nkv; a.hd = hd; a.n_kv = nkv; a.cap = c.cap;
     a.rope_base = c.rope_base; a.pos = pos; a.seq = seq; a.kc = kc; a.vc = vc; a.q_out = L.qkv;
+    for (int64_t i = 0; i < hd / 2; ++i)   // the RoPE frequencies, in fp64 on the host
+        a.rope_theta[i] = std::pow((double)c.rope_base, -2.0 * (double)i / (double)hd);
     if ((rc = launch_gemv(a, EPI_QKV, s, PRO_RMSNORM))) return rc;
     if ((rc = launch_attention(L.qkv, Nq, T, nq, nkv, hd, kc, vc, c.cap, pos, seq, nullptr, Nq,
-                               L.xq, L.xd, L.att_ws, L.att_bytes, true, s)))
+                               L.xq, L.xd, L.att_ws, L.att_bytes, s)))
         return rc;
     GemvArgs o = plain(w->w_o_q, w->w_o_d, H, Nq, T);
     o.xq = L.xq; o.xd = L.xd; o.y = x; o.residual = x;
@@ -120,7 +124,7 @@ int layer_prefill(const qk_layer* w, const qk_layer_cfg& c, float* x, int64_t T,
                              kc, vc, c.cap, s)))
         return rc;
     if ((rc = launch_attention(L.qkv, Nqkv, T, nq, nkv, hd, kc, vc, c.cap, pos, seq, nullptr, Nq,
-                               L.xq, L.xd, L.att_ws, L.att_bytes, false, s)))
+                               L.xq, L.xd, L.att_ws, L.att_bytes, s)))
         return rc;
     if ((rc = matmul(w->w_o_q, w->w_o_d, H, Nq, L.xq, L.xd, T, x, x, EPI_STORE, 0, s))) return rc;
     if ((rc = launch_rmsnorm_q8(x, w->gamma_ffn, T, H, c.eps, nullptr, L.xq, L.xd, s))) return rc;

@@ -265,7 +265,7 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     g.wq_gstride = 2 * F * (H / 2); g.wd_gstride = 2 * F * (H / QBLK);
     g.xq = w.xq; g.xd = w.xd; g.col_off = w.off; g.col_idx = w.col_tok;
     g.m = 0; g.groups = (int32_t)E; g.y = w.h; g.ldy = F; g.residual = nullptr; g.ldr = 0;
-    g.ffn = F; g.max_cols = 4;
+    g.ffn = F; g.max_cols = (int32_t)std::min<int64_t>(8, (P + E - 1) / E);
     rc = launch_gemv(g, EPI_SWIGLU, s);
     if (rc) return rc;
     rc = launch_quantize_q8(w.h, P, F, w.hq, w.hd, s);
@@ -276,7 +276,7 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     d.wq_gstride = H * (F / 2); d.wd_gstride = H * (F / QBLK);
     d.xq = w.hq; d.xd = w.hd; d.col_off = w.off; d.col_idx = nullptr;
     d.m = 0; d.groups = (int32_t)E; d.y = w.ys; d.ldy = H; d.residual = nullptr; d.ldr = 0;
-    d.ffn = 0; d.max_cols = 4;
+    d.ffn = 0; d.max_cols = g.max_cols;
     rc = launch_gemv(d, EPI_STORE, s);
     if (rc) return rc;
 
