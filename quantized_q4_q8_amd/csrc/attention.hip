@@ -133,9 +133,11 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
 // Merge pass: workgroup (head h, token t) combines the head's chunk records
 // by log-sum-exp rescaling, out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Thread (pair i, slice s) owns output dimensions 2i, 2i + 1 over chunks
-// s, s + SLICES, ...; all of its record loads are issued at once.  Slice sums
-// are added in slice order, so the result does not depend on timing.  Writes
-// the fp32 output and/or its Q8_0 codes (four lanes per block).
+// s, s + SLICES, ...; thread c also loads chunk c's (m, l).  Every load is
+// issued before anything waits; the chunk weights are then formed one per
+// thread.  Slice sums are added in slice order, so the result does not
+// depend on timing.  Writes the fp32 output and/or its Q8_0 codes (four
+// lanes per block).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ rec, int64_t nq,
                                                     int64_t nch, int64_t cap,
@@ -147,11 +149,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     constexpr int SLICES = 256 / PAIRS;
     constexpr int PER = (MAX_CHUNKS + SLICES - 1) / SLICES;
     __shared__ double wsh[MAX_CHUNKS];
-    __shared__ double red[SLICES];
+    __shared__ double red[4];
     __shared__ double2 acc_s[SLICES][PAIRS];
     __shared__ double res[HD];
     const int64_t h = blockIdx.x, t = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
     const int64_t col = h * HD;
     const bool valid = p >= 0 && p < cap;   // out-of-range position: zeros, no reads
@@ -159,43 +161,25 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
     const int pr = tid % PAIRS, sl = tid / PAIRS;
 
-    // every load of this thread at once: its chunks' (m, l) and output pair
-    double2 xv[PER], ml[PER];
+    // all loads first: chunk tid's (m, l) and this thread's output pairs
+    const double2 ml = tid < used ? *reinterpret_cast<const double2*>(hr + tid * (HD + 2))
+                                  : make_double2(-INFINITY, 0.0);
+    double2 xv[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         const int cc = sl + e * SLICES;
-        xv[e] = make_double2(0.0, 0.0);
-        ml[e] = make_double2(-INFINITY, 0.0);
-        if (cc < used) {
-            xv[e] = *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr);
-            if (pr == 0) ml[e] = *reinterpret_cast<const double2*>(hr + cc * (HD + 2));
-        }
+        xv[e] = cc < used ? *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr)
+                          : make_double2(0.0, 0.0);
     }
-    // M = max over chunks (slice maxima from the pair-0 threads)
-    double mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) mx = fmax(mx, ml[e].x);
-    if (pr == 0) red[sl] = mx;
+    double mx = group_max<WAVE>(ml.x);
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
-    double M = red[0];
-#pragma unroll
-    for (int q = 1; q < SLICES; ++q) M = fmax(M, red[q]);
-    __syncthreads();   // red is reused below
-    // chunk weights and the slice's share of the normalizer
-    if (pr == 0) {
-        double ls = 0.0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int cc = sl + e * SLICES;
-            if (cc < used) {
-                const double w = exp(ml[e].x - M);
-                wsh[cc] = w;
-                ls = fma(w, ml[e].y, ls);
-            }
-        }
-        red[sl] = ls;
-    }
-    __syncthreads();
+    mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    const double wc = tid < used ? exp(ml.x - mx) : 0.0;
+    if (tid < MAX_CHUNKS) wsh[tid] = wc;
+    const double ls = group_sum<WAVE>(wc * ml.y);
+    __syncthreads();   // everyone has read red[]; wsh is complete
+    if (lane == 0) red[wave] = ls;
     double a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -208,9 +192,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     acc_s[sl][pr] = make_double2(a0, a1);
     __syncthreads();
     if (tid < PAIRS) {
-        double lsum = 0.0, s0 = 0.0, s1 = 0.0;
+        const double lsum = (red[0] + red[1]) + (red[2] + red[3]);
+        double s0 = 0.0, s1 = 0.0;
         for (int q = 0; q < SLICES; ++q) {
-            lsum += red[q];
             s0 += acc_s[q][tid].x;
             s1 += acc_s[q][tid].y;
         }

@@ -24,21 +24,57 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 }
 
 // ---------------------------------------------------------- wave reductions
-// Butterfly over groups of W adjacent lanes (W a power of two <= 64).
-template <int W, typename T>
-__device__ __forceinline__ T group_sum(T v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Lane exchanges inside a row of 16 lanes go through DPP (a few cycles);
+// exchanges across rows through ds_bpermute.  DPP patterns: quad_perm
+// [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror (lane i of
+// 8 <-> 7 - i), row_mirror (lane i of 16 <-> 15 - i).  In a full reduction
+// the mirrors pair lanes from the two halves that already hold equal values,
+// so every lane of a group of W adjacent lanes ends with the group's total.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFF), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <typename T>
+struct SumOp {
+    __device__ static T f(T a, T b) { return a + b; }
+};
+template <typename T>
+struct MaxOp {
+    __device__ static T f(T a, T b) { return b > a ? b : a; }
+};
+
+// Reduction over groups of W adjacent lanes (W a power of two <= 64).
+template <int W, typename Op, typename T>
+__device__ __forceinline__ T group_reduce(T v) {
+    if (W >= 2) v = Op::f(v, dpp<DPP_XOR1>(v));
+    if (W >= 4) v = Op::f(v, dpp<DPP_XOR2>(v));
+    if (W >= 8) v = Op::f(v, dpp<DPP_HALF_MIRROR>(v));
+    if (W >= 16) v = Op::f(v, dpp<DPP_MIRROR>(v));
+    if (W >= 32) v = Op::f(v, __shfl_xor(v, 16, WAVE));
+    if (W >= 64) v = Op::f(v, __shfl_xor(v, 32, WAVE));
     return v;
 }
 template <int W, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+    return group_reduce<W, SumOp<T>>(v);
+}
+template <int W, typename T>
 __device__ __forceinline__ T group_max(T v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) {
-        const T u = __shfl_xor(v, o, WAVE);
-        v = u > v ? u : v;
-    }
-    return v;
+    return group_reduce<W, MaxOp<T>>(v);
 }
 
 // Arithmetic precision.  Activations and outputs are stored as fp32, but
@@ -104,8 +140,8 @@ __device__ __forceinline__ void q8_quad(const float v[8], uint32_t& lo, uint32_t
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+    amax = fmaxf(amax, dpp<DPP_XOR1>(amax));
+    amax = fmaxf(amax, dpp<DPP_XOR2>(amax));
     d = amax / 127.0f;
     uint32_t b[8];
 #pragma unroll
