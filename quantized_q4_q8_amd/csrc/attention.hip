@@ -112,15 +112,27 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
         __builtin_amdgcn_wave_barrier();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (lane < HD) {   // weighted values, lane = dimension
-            double o0 = 0.0, o1 = 0.0;
-            int r = 0;
-            for (; r + 1 < rows; r += 2) {
-                const double2 ee = *reinterpret_cast<const double2*>(&es[wave][r]);
-                o0 = fma(ee.x, (double)vs[r][lane], o0);
-                o1 = fma(ee.y, (double)vs[r + 1][lane], o1);
+            double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
+            if (rows == ACH) {   // full chunk: unrolled, LDS reads run ahead
+#pragma unroll
+                for (int r = 0; r < ACH; r += 4) {
+                    const double2 ea = *reinterpret_cast<const double2*>(&es[wave][r]);
+                    const double2 eb = *reinterpret_cast<const double2*>(&es[wave][r + 2]);
+                    o0 = fma(ea.x, (double)vs[r][lane], o0);
+                    o1 = fma(ea.y, (double)vs[r + 1][lane], o1);
+                    o2 = fma(eb.x, (double)vs[r + 2][lane], o2);
+                    o3 = fma(eb.y, (double)vs[r + 3][lane], o3);
+                }
+            } else {
+                int r = 0;
+                for (; r + 1 < rows; r += 2) {
+                    const double2 ee = *reinterpret_cast<const double2*>(&es[wave][r]);
+                    o0 = fma(ee.x, (double)vs[r][lane], o0);
+                    o1 = fma(ee.y, (double)vs[r + 1][lane], o1);
+                }
+                if (r < rows) o0 = fma(es[wave][r], (double)vs[r][lane], o0);
             }
-            if (r < rows) o0 = fma(es[wave][r], (double)vs[r][lane], o0);
-            rp[2 + lane] = o0 + o1;
+            rp[2 + lane] = (o0 + o1) + (o2 + o3);
         }
         if (lane == 0) {
             rp[0] = m;
