@@ -19,6 +19,7 @@ namespace {
 
 constexpr int ACH = 64;            // cache rows per chunk: one per lane
 constexpr int MAX_CHUNKS = 128;    // chunks per head (cap <= 8192)
+constexpr int64_t FLASH_MIN_TOKENS = 8;   // more tokens than this: the tiled pass
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -232,6 +233,170 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     }
 }
 
+// Many-token pass (prefill): workgroup (tile of TQ consecutive tokens, KV
+// head g) walks the KV chunks once for all tokens and all query heads of
+// the group, keeping a running (max, sum, output) per (token, head) row and
+// rescaling it as each chunk's scores arrive (the online form of the
+// max-subtracted softmax); nothing is written between chunks.  A tile is
+// processed in runs of consecutive tokens of the same sequence.  Wave w
+// takes query heads w, w + 8; lane = key for the scores, lane = output
+// dimension for the weighted sum.  fp64 throughout, K/V widened in LDS.
+template <int HD>
+__global__ __launch_bounds__(512) void k_attn_flash(
+    const float* __restrict__ q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, float* __restrict__ out,
+    int64_t o_ts, int8_t* __restrict__ oq, uint16_t* __restrict__ od) {
+    constexpr int TQ = 8;               // tokens per tile
+    constexpr int NW = 8;               // waves per workgroup
+    constexpr int MAXG = 512 / HD;      // query heads per group at most
+    constexpr int HPW = MAXG / NW;      // query heads per wave at most
+    __shared__ __align__(16) double qs[TQ][MAXG * HD];
+    __shared__ float ks[ACH][HD + 1];
+    __shared__ __align__(16) float vs[ACH][HD];
+    __shared__ __align__(16) double ps[NW][TQ][ACH];
+
+    const int64_t g = blockIdx.y, t0 = (int64_t)blockIdx.x * TQ;
+    const int G = (int)(nq / nkv);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ntile = (int)min((int64_t)TQ, tokens - t0);
+    const double rscale = sqrt((double)HD);
+
+    for (int i0 = 0; i0 < ntile;) {   // runs of one sequence (uniform)
+        const int s0 = seq[t0 + i0];
+        int i1 = i0 + 1;
+        while (i1 < ntile && seq[t0 + i1] == s0) ++i1;
+        const int nrun = i1 - i0;
+        int pi[TQ];
+        int kmax = -1;
+#pragma unroll
+        for (int i = 0; i < TQ; ++i) {
+            pi[i] = -1;
+            if (i < nrun) {
+                const int p = pos[t0 + i0 + i];
+                if (p >= 0 && p < cap) {   // out-of-range positions attend to nothing
+                    pi[i] = p;
+                    kmax = max(kmax, p);
+                }
+            }
+        }
+        __syncthreads();   // the previous run is done with qs
+        for (int idx = tid; idx < nrun * G * HD; idx += 512) {
+            const int i = idx / (G * HD), r = idx % (G * HD);
+            qs[i][r] = (double)q[(t0 + i0 + i) * q_ts + g * G * HD + r];
+        }
+
+        double m[HPW][TQ], l[HPW][TQ], o[HPW][TQ];
+#pragma unroll
+        for (int hp = 0; hp < HPW; ++hp)
+#pragma unroll
+            for (int i = 0; i < TQ; ++i) {
+                m[hp][i] = -INFINITY;
+                l[hp][i] = 0.0;
+                o[hp][i] = 0.0;
+            }
+
+        const int64_t cbase = (((int64_t)s0 * nkv + g) * cap) * HD;
+        for (int c = 0; c * ACH <= kmax; ++c) {
+            const int64_t r0 = (int64_t)c * ACH;
+            __syncthreads();   // ks/vs (and qs, first time) ready for rewriting / reading
+            for (int i = tid; i < ACH * HD / 8; i += 512) {
+                const int r = (i * 8) / HD, d = (i * 8) % HD;
+                uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+                if (r0 + r <= kmax) {
+                    kv = *reinterpret_cast<const uint4*>(kc + cbase + (r0 + r) * HD + d);
+                    vv = *reinterpret_cast<const uint4*>(vc + cbase + (r0 + r) * HD + d);
+                }
+                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ks[r][d + 2 * e] = h2f((uint16_t)(kw[e] & 0xFFFF));
+                    ks[r][d + 2 * e + 1] = h2f((uint16_t)(kw[e] >> 16));
+                    vs[r][d + 2 * e] = h2f((uint16_t)(vw[e] & 0xFFFF));
+                    vs[r][d + 2 * e + 1] = h2f((uint16_t)(vw[e] >> 16));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int hp = 0; hp < HPW; ++hp) {
+                const int hh = wave + hp * NW;
+                if (hh >= G) break;   // uniform over the wave
+                // scores of key r0 + lane for the run's tokens
+                double sc[TQ];
+#pragma unroll
+                for (int i = 0; i < TQ; ++i) sc[i] = 0.0;
+#pragma unroll 4
+                for (int d = 0; d < HD; d += 2) {
+                    const double k0 = (double)ks[lane][d], k1 = (double)ks[lane][d + 1];
+#pragma unroll
+                    for (int i = 0; i < TQ; ++i) {
+                        const double2 qq = *reinterpret_cast<const double2*>(&qs[i][hh * HD + d]);
+                        sc[i] = fma(qq.x, k0, sc[i]);
+                        sc[i] = fma(qq.y, k1, sc[i]);
+                    }
+                }
+                const int key = (int)r0 + lane;
+#pragma unroll
+                for (int i = 0; i < TQ; ++i) {
+                    const bool ok = key <= pi[i];   // pi = -1 for absent or out-of-range tokens
+                    const double s = ok ? sc[i] / rscale : -INFINITY;
+                    const double cm = group_max<WAVE>(s);
+                    double pv = 0.0;
+                    if (cm != -INFINITY) {   // uniform over the wave
+                        const double mn = fmax(m[hp][i], cm);
+                        const double f = exp(m[hp][i] - mn);   // 0 when m was -inf
+                        pv = ok ? exp(s - mn) : 0.0;
+                        l[hp][i] = fma(l[hp][i], f, group_sum<WAVE>(pv));
+                        o[hp][i] *= f;
+                        m[hp][i] = mn;
+                    }
+                    ps[wave][i][lane] = pv;
+                }
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane < HD) {   // weighted values, lane = dimension
+#pragma unroll 4
+                    for (int j = 0; j < ACH; j += 2) {
+                        const double v0 = (double)vs[j][lane], v1 = (double)vs[j + 1][lane];
+#pragma unroll
+                        for (int i = 0; i < TQ; ++i) {
+                            const double2 pp = *reinterpret_cast<const double2*>(&ps[wave][i][j]);
+                            o[hp][i] = fma(pp.x, v0, o[hp][i]);
+                            o[hp][i] = fma(pp.y, v1, o[hp][i]);
+                        }
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();   // ps is rewritten next
+            }
+        }
+
+        // outputs of the run: fp32 and/or Q8_0 (one 32-lane group per block)
+#pragma unroll
+        for (int hp = 0; hp < HPW; ++hp) {
+            const int hh = wave + hp * NW;
+            if (hh >= G) break;
+#pragma unroll
+            for (int i = 0; i < TQ; ++i) {
+                if (i >= nrun) break;
+                const float v = l[hp][i] > 0.0 ? (float)(o[hp][i] / l[hp][i]) : 0.0f;
+                const int64_t col = (t0 + i0 + i) * o_ts + (g * G + hh) * HD;
+                if (lane < HD) {
+                    if (out) out[col + lane] = v;
+                    if (oq) {
+                        const float amax = group_max<QBLK>(fabsf(v));
+                        const float d = amax / 127.0f;
+                        int qv = 0;
+                        if (d != 0.0f) qv = (int)fminf(127.0f, fmaxf(-127.0f, roundf(v / d)));
+                        oq[col + lane] = (int8_t)qv;
+                        if ((lane & (QBLK - 1)) == 0) od[(col + lane) / QBLK] = f2h(d);
+                    }
+                }
+            }
+        }
+        i0 = i1;
+    }
+}
+
 int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
                      int64_t hd, const uint16_t* kc, const uint16_t* vc, int64_t cap,
                      const int32_t* pos, const int32_t* seq, float* out, int64_t o_ts,
@@ -240,6 +405,18 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     if (!ws || ws_bytes < attention_ws_bytes(tokens, nq, nkv, hd, cap)) return QK_EWORKSPACE;
     const int64_t nch = (cap + ACH - 1) / ACH;
     if (nch > MAX_CHUNKS || (nq / nkv) * hd > 512) return QK_ESHAPE;
+    if (tokens > FLASH_MIN_TOKENS) {
+        dim3 fgrid((unsigned)((tokens + 7) / 8), (unsigned)nkv);
+        if (hd == 32)
+            hipLaunchKernelGGL(k_attn_flash<32>, fgrid, dim3(512), 0, s, q, q_ts, tokens, nq, nkv, kc,
+                               vc, cap, pos, seq, out, o_ts, oq, od);
+        else if (hd == 64)
+            hipLaunchKernelGGL(k_attn_flash<64>, fgrid, dim3(512), 0, s, q, q_ts, tokens, nq, nkv, kc,
+                               vc, cap, pos, seq, out, o_ts, oq, od);
+        else
+            return QK_ESHAPE;
+        return qk_launch_status();
+    }
     double* rec = static_cast<double*>(ws);
     dim3 grid((unsigned)nch, (unsigned)nkv, (unsigned)tokens);
     dim3 mgrid((unsigned)nq, (unsigned)tokens);

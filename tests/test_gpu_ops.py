@@ -251,6 +251,11 @@ ATT_CASES = [
     (3, 8, 8, 64, 130, 1, "mha"),
     (2, 16, 1, 32, 70, 2, "mqa"),
     (1, 32, 4, 64, 2176, 1, "first"),
+    # many tokens: the tiled pass (runs of one sequence inside 8-token tiles)
+    (64, 8, 2, 64, 200, 1, "prefill"),
+    (40, 32, 4, 64, 300, 3, "runs"),
+    (37, 16, 1, 32, 130, 2, "random"),
+    (12, 32, 4, 64, 2176, 1, "long"),
 ]
 
 
@@ -268,9 +273,15 @@ def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
         pos = np.array([0], np.int32)
     elif recipe == "ragged":
         pos = np.array([2175, 0, 63, 64, 1000, 129], np.int32)
+    elif recipe == "runs":   # sequences in runs of 14 tokens at consecutive positions
+        seq = (np.arange(tokens) // 14 % seqs).astype(np.int32)
+        pos = np.array([90 * (t // 14) + t % 14 + 3 for t in range(tokens)], np.int32)
+    elif recipe == "long":
+        pos = (2100 + np.arange(tokens)).astype(np.int32)
     else:
         pos = (synth.randint(111, 4, tokens, cap)).astype(np.int32)
-    seq = (np.arange(tokens) % seqs).astype(np.int32)
+    if recipe != "runs":
+        seq = (np.arange(tokens) % seqs).astype(np.int32)
     out = qk.gqa_attention(dev(q), dev(kc), dev(vc), dev(pos), dev(seq))
     ref = oracle.gqa_attention(q, kc, vc, pos, seq)
     assert rel_err(host(out), ref) < 1e-5
