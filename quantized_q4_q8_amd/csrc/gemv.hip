@@ -16,8 +16,7 @@
 // mask and a shift; v_dot4_i32_i8 forms the block's integer sum from the
 // unsigned nibbles and the int8 activations, and the -8 offset is applied
 // once per block as -8 * sum(x).  The wave's row sums are reduced together
-// by a transposed butterfly (tree_sum) and the epilogue runs in the lanes
-// that hold them.
+// (row_sums) and the epilogue runs in the lanes that hold them.
 #include "internal.h"
 
 namespace qk {
@@ -146,38 +145,49 @@ __device__ __forceinline__ void stage_row(const RowRegs<KC>& R, int64_t k, float
     }
 }
 
-// Sum of N values per lane over the 64 lanes of a wave, all N at once
-// ("transposed" butterfly): at each of the first log2(N) steps a lane keeps
-// half of its values and adds the partner's copy of them, so N sums cost
-// N - 1 + 6 - log2(N) exchanges instead of 6 N.  Afterwards lane l holds the
-// complete sum of value index tree_index<N>(l); the 64 / N lanes that differ
-// only in their low bits hold the same sum.  The order of additions is fixed,
-// so the result is deterministic.
+// Sums of N values per lane over the 64 lanes of a wave, all N at once.  Two
+// "transposed" butterfly steps across rows (lane offsets 32 and 16) halve
+// the value count each: a lane keeps the half its offset bit selects and adds
+// the partner's copy of it.  The remaining N / 4 values (at least one) are
+// then summed over the rest of the wave, ending with DPP steps inside each
+// 16-lane row, so every lane of a row holds the same complete sums.  Row
+// (b5, b4) of the wave (lane bits 5 and 4) holds value indices
+// b5 * N/2 + b4 * N/4 + k, k < max(N/4, 1) (for N < 4 the index is b5 when
+// N = 2, 0 when N = 1).  The order of additions is fixed, so the result is
+// deterministic.
 template <int N>
-__device__ __forceinline__ double tree_sum(double (&v)[N], int lane) {
-#pragma unroll
-    for (int h = N / 2, o = 32; h >= 1; h >>= 1, o >>= 1) {
-        const bool up = (lane & o) != 0;
+__device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
+    int base = 0;
+    if (N >= 2) {
+        constexpr int h = N / 2;
+        const bool up = (lane & 32) != 0;
 #pragma unroll
         for (int i = 0; i < h; ++i) {
             const double send = up ? v[i] : v[i + h];
             const double keep = up ? v[i + h] : v[i];
-            v[i] = keep + __shfl_xor(send, o, WAVE);
+            v[i] = keep + __shfl_xor(send, 32, WAVE);
         }
+        base += up ? h : 0;
     }
-    double s = v[0];
+    if (N >= 4) {
+        constexpr int h = N / 4;
+        const bool up = (lane & 16) != 0;
 #pragma unroll
-    for (int o = 32 / N; o >= 1; o >>= 1) s += __shfl_xor(s, o, WAVE);
-    return s;
-}
-
-template <int N>
-__device__ __forceinline__ int tree_index(int lane) {
-    int r = 0;
+        for (int i = 0; i < h; ++i) {
+            const double send = up ? v[i] : v[i + h];
+            const double keep = up ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, 16, WAVE);
+        }
+        base += up ? h : 0;
+    }
+    constexpr int NV = N >= 4 ? N / 4 : 1;
 #pragma unroll
-    for (int h = N / 2, o = 32; h >= 1; h >>= 1, o >>= 1)
-        if (lane & o) r += h;
-    return r;
+    for (int k = 0; k < NV; ++k) {
+        if (N == 1) v[k] += __shfl_xor(v[k], 32, WAVE);
+        if (N <= 2) v[k] += __shfl_xor(v[k], 16, WAVE);
+        v[k] = group_sum<16>(v[k]);
+    }
+    return base;
 }
 
 // Physical rows per output unit: SwiGLU units are (gate row, up row), QKV
@@ -205,7 +215,6 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     constexpr int P = rows_per_unit(EPI);
     static_assert(R % P == 0, "rows per wave must hold whole units");
     constexpr int N = RMAX * M;              // sums per lane in the reduction
-    constexpr int SPAN = WAVE / N;           // lanes holding the same sum
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int g = blockIdx.y;
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
         } else {
             // copy the Q8_0 columns into LDS: the first XREG chunks per thread
             // are loaded before the weights, the rest after
-            constexpr int XREG = M >= 4 ? 2 : 1;
+            constexpr int XREG = M == 1 ? 2 : (M == 2 ? 3 : 6);   // up to K = 6144 staged early
             const int64_t c16 = k / 16, tot = (int64_t)mc * c16, totd = (int64_t)mc * nb;
             // activation row of pass column m (m < mc), looked up per use
             const int32_t* __restrict__ cidx = a.col_idx;
@@ -362,10 +371,30 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int j = 0; j < RMAX; ++j) v[m * RMAX + j] = acc[j][m];
-        const double s = tree_sum<N>(v, lane);
-        const int r = tree_index<N>(lane);
+        const int base = row_sums<N>(v, lane);
+        // this lane's sum (index r) and, for two-row units, the unit's other
+        // row (index r ^ 1: the same lane when a row holds several sums, else
+        // the lane that differs in the last halving bit)
+        constexpr int NV = N >= 4 ? N / 4 : 1;
+        const int kk = NV > 1 ? (lane & 15) : 0;
+        double s = v[0], s2 = 0.0;
+#pragma unroll
+        for (int q = 1; q < NV; ++q)
+            if (kk == q) s = v[q];
+        if (P == 2) {
+            if (NV > 1) {
+                s2 = v[0];
+#pragma unroll
+                for (int q = 1; q < NV; ++q)
+                    if ((kk ^ 1) == q) s2 = v[q];
+            } else {
+                s2 = __shfl_xor(s, N == 4 ? 16 : 32, WAVE);
+            }
+        }
+        const int r = base + kk;
         const int m = r / RMAX, j = r % RMAX;
-        const bool owner = (lane & (SPAN - 1)) == 0 && rvalid(j) && cc + m < nc;
+        constexpr int OWN = N >= 4 ? 16 : (N == 2 ? 32 : 64);   // lanes sharing one row's sums
+        const bool owner = (NV > 1 ? kk < NV : (lane & (OWN - 1)) == 0) && rvalid(j) && cc + m < nc;
         const int64_t row = prow(j);
         const int64_t ocol = c0 + cc + m;
 
@@ -376,9 +405,6 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
                 a.y[ocol * a.ldy + row] = o;
             }
         } else if (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
-            // the unit's second row sits in the lane whose index differs in
-            // the bit that the last halving step decided
-            const double s2 = __shfl_xor(s, WAVE / N, WAVE);
             if (owner && (j % 2) == 0) {
                 const int64_t unit = unit0 + j / 2;
                 if (EPI == EPI_SWIGLU) {
@@ -491,11 +517,12 @@ size_t stage_bytes(int M, int64_t k) {
 // Physical rows per wave.  Kernels that stage their activations with a
 // fused RMSNorm prologue run two units per wave (fewer workgroups repeat the
 // prologue); the others one unit per wave until the launch has more than
-// 8192 units, then two, then four (two at most for 4 or 8 columns per pass).
+// 8192 units, then two, then four (two at most for 4 or 8 columns per pass
+// or rows longer than 64 blocks).
 // Small per-wave work and many waves keep the most loads in flight per CU.
-int pick_rows(int epi, int pro, int M, int64_t units) {
+int pick_rows(int epi, int pro, int M, int64_t k, int64_t units) {
     const int P = rows_per_unit(epi);
-    const int cap = M <= 2 ? 4 : 2;
+    const int cap = (M <= 2 && k / QBLK <= WAVE) ? 4 : 2;   // long rows hold more registers
     int upw = units > 2 * 8192 ? 4 : (units > 8192 ? 2 : 1);
     if (pro == PRO_RMSNORM && epi == EPI_SWIGLU && units >= 2048) upw = std::max(upw, 2);
     while (upw * P > cap) upw /= 2;
@@ -533,7 +560,7 @@ void launch_cfg(const GemvArgs& a, hipStream_t s) {
 template <int M, int U, int EPI, int PRO, int KC, bool KLOOP>
 void launch_r(const GemvArgs& a, hipStream_t s) {
     constexpr int P = rows_per_unit(EPI);
-    const int R = pick_rows(EPI, PRO, M, units_of(a, EPI) * a.groups);
+    const int R = pick_rows(EPI, PRO, M, a.k, units_of(a, EPI) * a.groups);
     if constexpr (M <= 2) {
         if (R >= 4) { launch_cfg<M, 4, U, EPI, PRO, KC, KLOOP>(a, s); return; }
     }
@@ -592,7 +619,7 @@ int64_t gemv_argmax_parts(int64_t n, int64_t k, int64_t max_cols) {
     GemvArgs a{};
     a.n = n; a.k = k; a.max_cols = (int32_t)max_cols; a.groups = 1;
     const int M = pick_cols(a, EPI_ARGMAX);
-    const int R = pick_rows(EPI_ARGMAX, PRO_RMSNORM, M, n);
+    const int R = pick_rows(EPI_ARGMAX, PRO_RMSNORM, M, k, n);
     const int64_t per_wg = 4 * (int64_t)(M <= 2 ? R : std::min(R, 2));
     return (n + per_wg - 1) / per_wg;
 }
