@@ -221,7 +221,7 @@ def run_decode(args):
     # weights, Q4_0; x and gamma fp32 read; h fp32 written
     kbytes = 2 * F * H * 9 / 16 + 2 * H * 4 + F * 4
     achieved = kbytes / (avg_us * 1e-6) / 1e9
-    kname = "k_gemv<1,64,4,1,EPI_SWIGLU,PRO_RMSNORM,1>"
+    kname = "k_gemv<1,4,1,EPI_SWIGLU,PRO_RMSNORM,1,false>"
     src = source_hash([os.path.join(ROOT, "quantized_q4_q8_amd", "csrc", f)
                        for f in ("gemv.hip", "internal.h", "common.h")])
     traffic = stored_traffic(kname, src)
