@@ -57,6 +57,8 @@ _SIGS = {
     "oracle_swiglu": ([_P, _P, _I64, _P], ctypes.c_int),
     "oracle_embed_lookup": ([_P, _I64, _I64, _P, _I64, _P], ctypes.c_int),
     "oracle_argmax": ([_P, _I64, _I64, _P], ctypes.c_int),
+    "oracle_sample": ([_P, _I64, _I64, ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, _P],
+                      ctypes.c_int),
     "oracle_layer_forward": ([ctypes.POINTER(Layer), ctypes.POINTER(LayerCfg), _P, _I64, _P, _P,
                               _P, _P], ctypes.c_int),
     "oracle_moe_route": ([_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P], ctypes.c_int),
@@ -235,6 +237,18 @@ def argmax(logits) -> np.ndarray:
     idx = np.empty(rows, np.int32)
     _check(lib().oracle_argmax(_p(logits), rows, vocab, _p(idx)), "argmax")
     return idx
+
+
+def sample(logits, top_k: int, top_p: float, temperature: float, u) -> np.ndarray:
+    """Sampler chain (top-k, top-p, temperature, draw with the given uniforms)."""
+    logits = _c(logits, np.float32)
+    vocab = logits.shape[-1]
+    rows = logits.size // vocab
+    u = _c(np.broadcast_to(np.asarray(u, np.float64), (rows,)), np.float64)
+    out = np.empty(rows, np.int32)
+    _check(lib().oracle_sample(_p(logits), rows, vocab, top_k, top_p, temperature, _p(u), _p(out)),
+           "sample")
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -426,6 +426,58 @@ int oracle_argmax(const float* logits, int64_t rows, int64_t vocab, int32_t* idx
     return OK;
 }
 
+// Sampler chain [GUIDE 8: temperature scales the probabilities, Top-K or
+// Top-P (nucleus) narrows the candidates, a random number picks the token;
+// LLAMACPP 5.4: the chain top-k, top-p (keeping at least one), temperature,
+// then a seeded draw].  Per row, with the caller's uniform u in [0, 1):
+//  1. rank every id by logit, largest first, equal logits by lower id; keep
+//     the first top_k;
+//  2. p_i = exp(l_i - l_0) / sum_kept exp(l_j - l_0); keep the shortest rank
+//     prefix whose running sum of p reaches top_p (at least one id);
+//  3. w_i = exp((l_i - l_0) / temperature) over the kept ids;
+//  4. the token is the first kept id (in rank order) whose running sum of w
+//     exceeds u * sum w (the last kept id if rounding leaves none).
+// temperature <= 0 is greedy: the rank-0 id.  Sums run in rank order in fp64.
+int oracle_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, float top_p,
+                  float temperature, const double* u, int32_t* out) {
+    if (vocab <= 0 || top_k <= 0) return E_SHAPE;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* l = logits + r * vocab;
+        std::vector<int32_t> ids((size_t)vocab);
+        for (int64_t i = 0; i < vocab; ++i) ids[(size_t)i] = (int32_t)i;
+        std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b) { return l[a] > l[b]; });
+        const int64_t k = std::min<int64_t>(top_k, vocab);
+        if (temperature <= 0.0f) {
+            out[r] = ids[0];
+            continue;
+        }
+        const double l0 = (double)l[ids[0]];
+        double s1 = 0.0;
+        for (int64_t i = 0; i < k; ++i) s1 += std::exp((double)l[ids[(size_t)i]] - l0);
+        int64_t keep = 0;
+        double cum = 0.0;
+        while (keep < k) {
+            cum += std::exp((double)l[ids[(size_t)keep]] - l0) / s1;
+            ++keep;
+            if (cum >= (double)top_p) break;
+        }
+        double wsum = 0.0;
+        for (int64_t i = 0; i < keep; ++i) wsum += std::exp(((double)l[ids[(size_t)i]] - l0) / (double)temperature);
+        const double target = u[r] * wsum;
+        int32_t pick = ids[(size_t)(keep - 1)];
+        double cw = 0.0;
+        for (int64_t i = 0; i < keep; ++i) {
+            cw += std::exp(((double)l[ids[(size_t)i]] - l0) / (double)temperature);
+            if (cw > target) {
+                pick = ids[(size_t)i];
+                break;
+            }
+        }
+        out[r] = pick;
+    }
+    return OK;
+}
+
 // One pre-norm LLaMA decoder layer [GUIDE 5.2 figure: norm -> Q/K/V -> RoPE
 // -> KV store/load -> attention -> scale and softmax -> output projection ->
 // residual; GUIDE 4.4 for the FFN half]:

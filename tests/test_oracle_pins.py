@@ -591,3 +591,58 @@ def test_expert_ffn_fp64_bruteforce():
     h = g[:F] / (1 + np.exp(-g[:F])) * g[F:]
     ref = deq(c, d) @ _np_q8(h[None].astype(np.float32))[0]
     assert np.allclose(y, ref, rtol=1e-4, atol=1e-6)
+
+
+# ---------------------------------------------------------------- sampler chain
+def test_sampler_golden_worked_example():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "sampler_chain.json")))
+    for c in g["cases"]:
+        got = oracle.sample(np.array(c["logits"], np.float32), c["top_k"], c["top_p"], c["temperature"], [c["u"]])
+        assert int(got[0]) == c["token"], c
+
+
+def test_sampler_greedy_limits_equal_argmax():
+    """top_k = 1, or temperature 0, or top_p tiny: the argmax for every u."""
+    logits = synth.normal(120, 1, (6, 300)) * np.float32(3.0)
+    logits[2, 10] = logits[2, 200] = 50.0               # tie: the lower id
+    want = oracle.argmax(logits)
+    for u in (0.0, 0.37, 0.999999):
+        assert np.array_equal(oracle.sample(logits, 1, 0.9, 0.7, u), want)
+        assert np.array_equal(oracle.sample(logits, 40, 0.9, 0.0, u), want)
+        assert np.array_equal(oracle.sample(logits, 40, 1e-9, 1.5, u), want)
+
+
+def _grid_counts(logits, top_k, top_p, temp, n=20000):
+    u = (np.arange(n) + 0.5) / n
+    toks = oracle.sample(np.tile(logits, (n, 1)), top_k, top_p, temp, u)
+    return np.bincount(toks, minlength=logits.size) / n
+
+
+def test_sampler_draw_is_softmax_at_temperature():
+    """With every id kept, the inverse-CDF draw over a uniform grid of u
+    reproduces softmax(l / T) (scipy) to within the grid spacing per id."""
+    from scipy.special import softmax
+    logits = (synth.normal(121, 1, 37) * np.float32(1.3)).astype(np.float32)
+    for temp in (1.0, 2.0, 0.7):
+        freq = _grid_counts(logits, 37, 1.0, temp)
+        ref = softmax(logits.astype(np.float64) / temp)
+        assert np.max(np.abs(freq - ref)) <= 1.0 / 20000 + 1e-12
+
+
+def test_sampler_top_p_and_top_k_truncation():
+    """Probabilities 0.5, 0.3, 0.15, 0.05: top_p = 0.75 keeps the first two,
+    which are then drawn with weights 0.625 / 0.375; top_k = 3 with top_p = 1
+    renormalizes the first three."""
+    p = np.array([0.05, 0.5, 0.15, 0.3])                 # ids 1, 3, 2, 0 by rank
+    logits = np.log(p).astype(np.float32)
+    freq = _grid_counts(logits, 4, 0.75, 1.0)
+    assert abs(freq[1] - 0.625) <= 1e-4 and abs(freq[3] - 0.375) <= 1e-4 and freq[0] == freq[2] == 0
+    freq = _grid_counts(logits, 3, 1.0, 1.0)
+    assert freq[0] == 0 and abs(freq[1] - 0.5 / 0.95) <= 1e-4 and abs(freq[2] - 0.15 / 0.95) <= 1e-4
+
+
+def test_sampler_ties_keep_lowest_ids():
+    logits = np.zeros(100, np.float32)
+    freq = _grid_counts(logits, 2, 1.0, 1.0, n=1000)
+    assert abs(freq[0] - 0.5) <= 1e-3 and abs(freq[1] - 0.5) <= 1e-3 and freq[2:].sum() == 0
