@@ -38,9 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode", choices=["decode", "matmul", "prefill", "moe"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "matmul", "prefill", "moe", "sample"],
                     help="decode (the headline line); the others measure the standalone matmul, "
-                         "prefill and MoE workloads")
+                         "prefill, MoE and sampler workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -552,6 +552,42 @@ def run_moe(args):
     print(json.dumps(out), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# sampler chain over the LM-head logits (vocab 32000): top-k 40, top-p 0.9,
+# temperature 0.7, one uniform per row
+# ---------------------------------------------------------------------------
+def run_sample(args):
+    import numpy as np
+    import torch
+
+    import quantized_q4_q8_amd as qk
+    from synth import normal, randint
+
+    V, L = 32000, 22
+    dev = torch.device("cuda")
+    rows_out = []
+    for rows in (1, 8):
+        lg = [torch.from_numpy(normal(5, 200 + i, (rows, V)) * np.float32(2.5)).to(dev) for i in range(L)]
+        u = torch.from_numpy((randint(5, 300, rows, 1 << 30).astype(np.float64) + 0.5) / (1 << 30)).to(dev)
+        ids = torch.empty(rows, dtype=torch.int32, device=dev)
+        us = graph_time_us(lambda: [qk.qk_sample(x, 40, 0.9, 0.7, u, out=ids) for x in lg], L,
+                           max(5, args.steps))
+        nbytes = rows * V * 4
+        rows_out.append({"rows": rows, "us_per_call": round(us, 3), "GBps": round(nbytes / us / 1e3, 1)})
+        log(f"sample rows={rows}: {us:.2f} us per call")
+    head = rows_out[0]
+    out = base_line(args, "sampler calls/s (32000 logits, top-k 40, top-p 0.9, temperature 0.7)",
+                    1e6 / head["us_per_call"], "calls/s", head["us_per_call"] / 1e3,
+                    "fp32 logits, fp64 weights and sums",
+                    {"workload": "sampler chain over one 32000-logit row (and 8 rows)",
+                     "parallelism": "single GPU"})
+    out["roofline"] = {"bound": "hbm", "kernel": "k_sample", "achieved": head["GBps"],
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(head["GBps"] / HBM_PEAK_GBS, 5),
+                       "traffic": None, "bytes_per_launch": V * 4, "avg_us": head["us_per_call"]}
+    out["rows"] = rows_out
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -565,7 +601,7 @@ def main():
         sys.exit(1)
     import quantized_q4_q8_amd as qk
     qk.load()
-    {"decode": run_decode, "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe}[args.workload](args)
+    {"decode": run_decode, "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
 
 
 if __name__ == "__main__":

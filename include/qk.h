@@ -157,6 +157,31 @@ int qk_embed_lookup(const float* table, int64_t vocab, int64_t hidden, const int
 int qk_argmax(const float* logits, int64_t rows, int64_t vocab, int32_t* idx, void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Sampling                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* Sampler chain [TinyLLaMA-in-C++ guide 8: temperature, Top-K or Top-P,
+ * then a random number picks the token; llama.cpp guide 5.4: the chain
+ * top-k, top-p keeping at least one, temperature, seeded draw].  Per row of
+ * logits [rows][vocab] (fp32, finite):
+ *  1. rank the ids by logit, largest first, equal logits by lower id, and keep
+ *     the first top_k (1 <= top_k <= 256);
+ *  2. p_i = exp(l_i - l_0) / sum over the kept exp(l_j - l_0) (fp64); keep the
+ *     shortest rank prefix whose running sum of p reaches top_p (at least one);
+ *  3. w_i = exp((l_i - l_0) / temperature) over the kept ids;
+ *  4. ids[row] = the first kept id, in rank order, whose running sum of w
+ *     exceeds u[row] * sum w, with the caller's uniform u[row] in [0, 1) (fp64,
+ *     device); the last kept id if rounding leaves none.
+ * temperature <= 0 gives the rank-0 id (greedy).  The sums are fp64 but
+ * taken as a tree, so a u within about 1e-12 of a boundary of the running
+ * sums (or a top_p that close to a running probability) may fall either way.
+ * logits and ids are device memory, top_p is used at float precision.  No
+ * workspace.  Returns QK_EINVAL for top_k outside [1, 256], QK_ESHAPE for
+ * vocab > 32768. */
+int qk_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, float top_p,
+              float temperature, const double* u, int32_t* ids, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* Attention                                                              */
 /* ---------------------------------------------------------------------- */
 

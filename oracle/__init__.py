@@ -57,7 +57,7 @@ _SIGS = {
     "oracle_swiglu": ([_P, _P, _I64, _P], ctypes.c_int),
     "oracle_embed_lookup": ([_P, _I64, _I64, _P, _I64, _P], ctypes.c_int),
     "oracle_argmax": ([_P, _I64, _I64, _P], ctypes.c_int),
-    "oracle_sample": ([_P, _I64, _I64, ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, _P],
+    "oracle_sample": ([_P, _I64, _I64, ctypes.c_int32, ctypes.c_double, ctypes.c_float, _P, _P],
                       ctypes.c_int),
     "oracle_layer_forward": ([ctypes.POINTER(Layer), ctypes.POINTER(LayerCfg), _P, _I64, _P, _P,
                               _P, _P], ctypes.c_int),
@@ -239,8 +239,12 @@ def argmax(logits) -> np.ndarray:
     return idx
 
 
-def sample(logits, top_k: int, top_p: float, temperature: float, u) -> np.ndarray:
-    """Sampler chain (top-k, top-p, temperature, draw with the given uniforms)."""
+def sample(logits, top_k: int, top_p: float, temperature: float, u, top_p_shift: float = 0.0) -> np.ndarray:
+    """Sampler chain (top-k, top-p, temperature, draw with the given uniforms).
+
+    top_p is taken at float32, as the library takes it; top_p_shift moves the
+    cut by a small amount past that value (to probe a boundary)."""
+    top_p = float(np.float32(top_p)) + top_p_shift
     logits = _c(logits, np.float32)
     vocab = logits.shape[-1]
     rows = logits.size // vocab

@@ -438,7 +438,7 @@ int oracle_argmax(const float* logits, int64_t rows, int64_t vocab, int32_t* idx
 //  4. the token is the first kept id (in rank order) whose running sum of w
 //     exceeds u * sum w (the last kept id if rounding leaves none).
 // temperature <= 0 is greedy: the rank-0 id.  Sums run in rank order in fp64.
-int oracle_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, float top_p,
+int oracle_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, double top_p,
                   float temperature, const double* u, int32_t* out) {
     if (vocab <= 0 || top_k <= 0) return E_SHAPE;
     for (int64_t r = 0; r < rows; ++r) {
@@ -459,7 +459,7 @@ int oracle_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_
         while (keep < k) {
             cum += std::exp((double)l[ids[(size_t)keep]] - l0) / s1;
             ++keep;
-            if (cum >= (double)top_p) break;
+            if (cum >= top_p) break;
         }
         double wsum = 0.0;
         for (int64_t i = 0; i < keep; ++i) wsum += std::exp(((double)l[ids[(size_t)i]] - l0) / (double)temperature);

@@ -58,6 +58,8 @@ _SIGS = {
     "swiglu": ([_P, _P, _I64, _P, _P], ctypes.c_int),
     "qk_kv_append": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "qk_embed_lookup": ([_P, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "qk_sample": ([_P, _I64, _I64, ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, _P, _P],
+                  ctypes.c_int),
     "qk_argmax": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "gqa_attention": ([_P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P],
                       ctypes.c_int),
@@ -261,6 +263,17 @@ def qk_embed_lookup(table, ids, out=None):
                                   _dev(ids, torch.int32, "ids"), ids.numel(),
                                   _dev(x, torch.float32, "x"), _stream()), "qk_embed_lookup")
     return x
+
+
+def qk_sample(logits, top_k: int, top_p: float, temperature: float, u, out=None):
+    """Sampler chain over logits [rows][vocab] with uniforms u [rows] (fp64) -> ids."""
+    vocab = logits.shape[-1]
+    rows = logits.numel() // vocab
+    ids = _out(out, (rows,), torch.int32, logits)
+    _check(load().qk_sample(_dev(logits, torch.float32, "logits"), rows, vocab, top_k, top_p,
+                            temperature, _dev(u, torch.float64, "u"), _dev(ids, torch.int32, "ids"),
+                            _stream()), "qk_sample")
+    return ids
 
 
 def qk_argmax(logits, out=None):

@@ -314,3 +314,78 @@ def test_error_codes_and_nothing_enqueued(gpu_lib):
     torch.cuda.synchronize()
     # nothing was enqueued: outputs untouched
     assert torch.all(q == 5) and torch.all(d == 3) and torch.all(out == 9.0)
+
+
+# ---------------------------------------------------------------- sampler chain
+def _sample_agrees(qk_ids, logits, top_k, top_p, temp, u):
+    """GPU ids equal the oracle's, except where u lies within 1e-9 of a
+    cumulative boundary or the top-p cut within 1e-12 of a running
+    probability: there the fp64 exp and the order of the fp64 sums of either
+    side may decide."""
+    want = oracle.sample(logits, top_k, top_p, temp, u)
+    for r in np.nonzero(qk_ids != want)[0]:
+        alt = {int(oracle.sample(logits[r], top_k, top_p, temp, [min(u[r] + d, 1 - 1e-16)])[0])
+               for d in (-1e-9, 1e-9)}
+        alt |= {int(oracle.sample(logits[r], top_k, top_p, temp, [u[r]], top_p_shift=d)[0]) for d in (-1e-12, 1e-12)}
+        assert int(qk_ids[r]) in alt, f"row {r}: {qk_ids[r]} vs {want[r]}"
+    return float(np.mean(qk_ids == want))
+
+
+@pytest.mark.parametrize("rows,vocab,top_k,top_p,temp", [
+    (8, 32000, 40, 0.9, 0.7),      # the chain of the llama.cpp guide
+    (5, 32000, 256, 1.0, 1.0),
+    (7, 1000, 1, 0.9, 0.7),        # greedy by top-k
+    (6, 517, 13, 0.5, 1.7),
+    (4, 32000, 40, 0.9, 0.0),      # greedy by temperature
+    (3, 5001, 40, 0.9, 0.7),       # rows not a multiple of 4 logits: 4-byte loads
+    (3, 3000, 256, 0.95, 1.3),     # between 1024 and 4096 logits
+    (2, 32768, 40, 0.9, 0.7),      # the largest row
+])
+def test_sampler_chain(gpu_lib, rows, vocab, top_k, top_p, temp):
+    qk = gpu_lib
+    say(f"qk_sample rows={rows} vocab={vocab} k={top_k} p={top_p} T={temp}")
+    logits = synth.normal(130, rows + vocab, (rows, vocab)) * np.float32(2.5)
+    logits[0, 5] = logits[0, 900 % vocab] = np.float32(40.0)   # a tie at the top
+    u = (synth.randint(130, 1, rows, 1 << 30).astype(np.float64) + 0.5) / (1 << 30)
+    ids = host(qk.qk_sample(dev(logits), top_k, top_p, temp, dev(u)))
+    assert _sample_agrees(ids, logits, top_k, top_p, temp, u) >= 0.99
+
+
+def test_sampler_ties_and_grid(gpu_lib):
+    """All-equal logits keep the lowest ids; a grid of u reproduces the
+    oracle's draws token for token."""
+    qk = gpu_lib
+    say("qk_sample ties and u grid")
+    flat = np.zeros((3, 300), np.float32)
+    u = np.array([0.1, 0.5, 0.9])
+    assert host(qk.qk_sample(dev(flat), 4, 1.0, 1.0, dev(u))).tolist() == [0, 2, 3]
+    logits = np.tile(synth.normal(131, 1, 64) * np.float32(1.5), (400, 1)).astype(np.float32)
+    ug = (np.arange(400) + 0.5) / 400
+    ids = host(qk.qk_sample(dev(logits), 64, 0.95, 0.8, dev(ug)))
+    assert _sample_agrees(ids, logits, 64, 0.95, 0.8, ug) >= 0.99
+
+
+@pytest.mark.parametrize("levels,top_k", [(4, 256), (4, 40), (50, 256), (50, 7)])
+def test_sampler_heavy_ties(gpu_lib, levels, top_k):
+    """Integer-valued logits over 32000 ids: thousands of ids share the top
+    value (levels 4), or a few hundred do (levels 50).  The kept set is the
+    lowest ids among equal logits in both regimes."""
+    qk = gpu_lib
+    say(f"qk_sample heavy ties levels={levels} k={top_k}")
+    rows, vocab = 4, 32000
+    logits = synth.randint(132, levels, (rows, vocab), levels).astype(np.float32)
+    u = (synth.randint(133, 1, rows, 1 << 30).astype(np.float64) + 0.5) / (1 << 30)
+    for temp in (0.0, 0.7):
+        ids = host(qk.qk_sample(dev(logits), top_k, 0.9, temp, dev(u)))
+        assert _sample_agrees(ids, logits, top_k, 0.9, temp, u) >= 0.99
+
+
+def test_sampler_rejects_bad_top_k(gpu_lib):
+    qk = gpu_lib
+    L = qk.load()
+    x = torch.zeros((1, 10), dtype=torch.float32, device="cuda")
+    u = torch.zeros(1, dtype=torch.float64, device="cuda")
+    o = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.qk_sample(x.data_ptr(), 1, 10, 0, 0.9, 0.7, u.data_ptr(), o.data_ptr(), s) == qk.QK_EINVAL
+    assert L.qk_sample(x.data_ptr(), 1, 10, 257, 0.9, 0.7, u.data_ptr(), o.data_ptr(), s) == qk.QK_EINVAL
