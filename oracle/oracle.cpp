@@ -42,6 +42,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <vector>
 
 namespace {
@@ -233,12 +234,14 @@ void rope(float* x, int64_t tokens, int64_t heads, int64_t hd, const int32_t* po
 // KV store [GUIDE 7]: the step's K and V rows go to row pos of the
 // preallocated fp16 cache of their sequence.  Cache layout
 // [seqs][n_kv][cap][hd].
+// The cache of a sequence is a ring of cap rows [ENGINE 8: sized once for the
+// longest context and used as a ring buffer]: position p lives in row p % cap.
 void kv_append(const float* k, const float* v, int64_t tokens, int64_t n_kv, int64_t hd,
                const int32_t* pos, const int32_t* seq, uint16_t* kc, uint16_t* vc, int64_t cap) {
     for (int64_t t = 0; t < tokens; ++t)
         for (int64_t g = 0; g < n_kv; ++g)
             for (int64_t d = 0; d < hd; ++d) {
-                const int64_t dst = (((int64_t)seq[t] * n_kv + g) * cap + pos[t]) * hd + d;
+                const int64_t dst = (((int64_t)seq[t] * n_kv + g) * cap + pos[t] % cap) * hd + d;
                 kc[dst] = float_to_half(k[(t * n_kv + g) * hd + d]);
                 vc[dst] = float_to_half(v[(t * n_kv + g) * hd + d]);
             }
@@ -246,8 +249,10 @@ void kv_append(const float* k, const float* v, int64_t tokens, int64_t n_kv, int
 
 // Scaled dot-product attention with GQA [ENGINE 8; GUIDE 4.3, 7]: query
 // head h reads KV head g = h / (nq / nkv); token t at position p attends to
-// cache rows 0..p of its sequence; s_j = q.k_j / sqrt(hd); softmax with the
-// maximum subtracted; o = sum_j p_j v_j.
+// positions max(0, p - cap + 1)..p of its sequence, which are cache rows
+// 0..min(p, cap - 1) of the ring (their order does not matter to the sum);
+// s_j = q.k_j / sqrt(hd); softmax with the maximum subtracted;
+// o = sum_j p_j v_j.
 void attention(const float* q, int64_t tokens, int64_t nq, int64_t nkv, int64_t hd,
                const uint16_t* kc, const uint16_t* vc, int64_t cap, const int32_t* pos,
                const int32_t* seq, float* out) {
@@ -256,7 +261,7 @@ void attention(const float* q, int64_t tokens, int64_t nq, int64_t nkv, int64_t 
     for (int64_t t = 0; t < tokens; ++t) {
         for (int64_t h = 0; h < nq; ++h) {
             const int64_t g = h / group;
-            const int64_t n = (int64_t)pos[t] + 1;
+            const int64_t n = std::min((int64_t)pos[t] + 1, cap);
             const uint16_t* K = kc + ((int64_t)seq[t] * nkv + g) * cap * hd;
             const uint16_t* V = vc + ((int64_t)seq[t] * nkv + g) * cap * hd;
             const float* qh = q + (t * nq + h) * hd;
@@ -291,9 +296,20 @@ void swiglu(const float* gate, const float* up, int64_t n, float* h) {
     }
 }
 
+// Positions are non-negative.  A call holding more than one token of a
+// sequence keeps that sequence's positions below cap: past the wrap, a later
+// token's row would overwrite a position an earlier token of the same call
+// still attends to.
 bool valid_pos_seq(const int32_t* pos, const int32_t* seq, int64_t tokens, int64_t cap) {
-    for (int64_t t = 0; t < tokens; ++t)
-        if (pos[t] < 0 || pos[t] >= cap || seq[t] < 0) return false;
+    std::map<int32_t, std::pair<int64_t, int32_t>> per_seq;   // seq -> (tokens, max pos)
+    for (int64_t t = 0; t < tokens; ++t) {
+        if (pos[t] < 0 || seq[t] < 0) return false;
+        auto& e = per_seq[seq[t]];
+        e.first += 1;
+        e.second = std::max(e.second, pos[t]);
+    }
+    for (const auto& kv : per_seq)
+        if (kv.second.first > 1 && kv.second.second >= cap) return false;
     return true;
 }
 

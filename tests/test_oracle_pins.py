@@ -360,6 +360,53 @@ def test_attention_fp64_bruteforce():
             assert np.allclose(o[t, h], p @ Vt, rtol=1e-6, atol=1e-7)
 
 
+def test_ring_cache_decode_is_sliding_window_bruteforce():
+    """ENGINE 8 (the KV arena holds the longest context and is used as a ring
+    buffer): decoding past cap one token at a time, position p sits in row
+    p % cap, and attention at p equals softmax attention over the positions
+    p - cap + 1 .. p of the whole history, brute force in fp64."""
+    from scipy.special import softmax
+    nq, nkv, hd, cap, steps = 4, 2, 32, 8, 21
+    ks = synth.normal(30, 1, (steps, nkv, hd))
+    vs = synth.normal(30, 2, (steps, nkv, hd))
+    qs = synth.normal(30, 3, (steps, nq, hd))
+    kc = np.zeros((1, nkv, cap, hd), np.uint16)
+    vc = np.zeros_like(kc)
+    seq = np.zeros(1, np.int32)
+    Kh = ks.astype(np.float16).astype(np.float64)   # the history as the cache stores it
+    Vh = vs.astype(np.float16).astype(np.float64)
+    for p in range(steps):
+        pos = np.array([p], np.int32)
+        oracle.kv_append(ks[p:p + 1], vs[p:p + 1], pos, seq, kc, vc)
+        assert np.array_equal(kc[0, :, p % cap], ks[p].astype(np.float16).view(np.uint16))
+        o = oracle.gqa_attention(qs[p:p + 1], kc, vc, pos, seq)
+        lo = max(0, p - cap + 1)
+        for h in range(nq):
+            g = h // (nq // nkv)
+            w = softmax(Kh[lo:p + 1, g] @ qs[p, h].astype(np.float64) / np.sqrt(hd))
+            assert np.allclose(o[0, h], w @ Vh[lo:p + 1, g], rtol=1e-6, atol=1e-7), (p, h)
+
+
+def test_ring_cache_rejects_multi_token_wrap():
+    """Past the wrap, a call holding several tokens of one sequence would
+    overwrite rows its own earlier tokens attend to: such calls are
+    rejected; one token per sequence is accepted at any position."""
+    nkv, hd, cap = 1, 32, 8
+    kc = np.zeros((2, nkv, cap, hd), np.uint16)
+    vc = np.zeros_like(kc)
+    k = synth.normal(31, 1, (2, nkv, hd))
+    q = synth.normal(31, 2, (2, 2, hd))
+    oracle.kv_append(k, k, np.array([6, 7], np.int32), np.array([0, 0], np.int32), kc, vc)
+    oracle.kv_append(k, k, np.array([100, 9], np.int32), np.array([0, 1], np.int32), kc, vc)
+    assert np.array_equal(kc[0, 0, 100 % cap], k[0, 0].astype(np.float16).view(np.uint16))
+    with pytest.raises(ValueError):
+        oracle.kv_append(k, k, np.array([7, 8], np.int32), np.array([0, 0], np.int32), kc, vc)
+    with pytest.raises(ValueError):
+        oracle.gqa_attention(q, kc, vc, np.array([8, 9], np.int32), np.array([1, 1], np.int32))
+    with pytest.raises(ValueError):
+        oracle.kv_append(k, k, np.array([-1, 0], np.int32), np.array([0, 1], np.int32), kc, vc)
+
+
 # ---------------------------------------------------------------------------
 # embedding, argmax
 # ---------------------------------------------------------------------------
