@@ -138,11 +138,12 @@ int rope(float* x, int64_t tokens, int64_t heads, int64_t head_dim, const int32_
  * gate, up, h: n fp32 each. */
 int swiglu(const float* gate, const float* up, int64_t n, float* h, void* stream);
 
-/* KV store [GUIDE 7]: k_cache[seq[t]][g][pos[t]][:] = fp16(k[t][g][:]) and
- * likewise for v.  k, v [tokens][n_kv][hd] fp32; caches fp16
- * [seqs][n_kv][cap][hd]; pos, seq int32 [tokens] (device).  pos must be in
- * [0, cap) and seq must name an existing sequence (not checked on the
- * device: the caller owns the cache bounds). */
+/* KV store [GUIDE 7; ENGINE 8, the cache as a ring buffer]:
+ * k_cache[seq[t]][g][pos[t] % cap][:] = fp16(k[t][g][:]) and likewise for v.
+ * k, v [tokens][n_kv][hd] fp32; caches fp16 [seqs][n_kv][cap][hd]; pos, seq
+ * int32 [tokens] (device).  pos >= 0 (negative rows are skipped); past cap
+ * the row of position pos - cap is overwritten.  seq must name an existing
+ * sequence (not checked on the device: the caller owns the cache bounds). */
 int qk_kv_append(const float* k, const float* v, int64_t tokens, int64_t n_kv, int64_t hd,
                  const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,
                  int64_t cap, void* stream);
@@ -187,12 +188,14 @@ int qk_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, f
 
 /* Grouped-query attention over an fp16 KV cache [ENGINE 8; GUIDE 4.3, 7].
  * Query head h of token t reads KV head g = h / (n_q_heads / n_kv_heads) of
- * sequence seq[t] and attends to cache rows 0..pos[t] (inclusive):
+ * sequence seq[t] and attends to positions max(0, pos - cap + 1)..pos
+ * (inclusive), i.e. ring rows 0..min(pos[t], cap - 1):
  * s_j = q . k_j / sqrt(head_dim), p = softmax(s), out = sum_j p_j v_j.
  * q, out [tokens][n_q_heads][head_dim] fp32; caches fp16
- * [seqs][n_kv_heads][cap][head_dim]; pos, seq int32 [tokens] (device, pos in
- * [0, cap)).  head_dim must be 32 or 64 and n_q_heads / n_kv_heads at most
- * 512 / head_dim.  ws: qk_gqa_attention_workspace() bytes. */
+ * [seqs][n_kv_heads][cap][head_dim]; pos, seq int32 [tokens] (device,
+ * pos >= 0; a negative position gives zeros).  head_dim must be 32 or 64 and
+ * n_q_heads / n_kv_heads at most 512 / head_dim.  ws:
+ * qk_gqa_attention_workspace() bytes. */
 int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads, int64_t n_kv_heads,
                   int64_t head_dim, const uint16_t* k_cache, const uint16_t* v_cache,
                   int64_t cap, const int32_t* pos, const int32_t* seq, float* out, void* ws,
@@ -231,13 +234,18 @@ typedef struct qk_layer_cfg {
 
 /* One pre-norm LLaMA decoder layer [GUIDE 5.2 figure; GUIDE 4.1-4.4]:
  *   u  = rmsnorm(x, gamma_attn); [q|k|v] = w_qkv . Q8_0(u)
- *   q, k = rope(q, k, pos); k, v -> cache rows pos of seq
+ *   q, k = rope(q, k, pos); k, v -> cache rows pos % cap of seq
  *   x1 = x + w_o . Q8_0(gqa_attention(q, cache))
  *   u1 = rmsnorm(x1, gamma_ffn); [g|up] = w_gate_up . Q8_0(u1)
  *   x2 = x1 + w_down . Q8_0(swiglu(g, up))
  * x [tokens][hidden] fp32 is updated in place to x2.  Tokens may belong to
- * different sequences; each token attends causally to rows 0..pos[t] of its
- * sequence, which includes the rows this call writes.  cap <= 8192.
+ * different sequences; each token attends causally to positions
+ * max(0, pos - cap + 1)..pos[t] of its sequence, which includes the rows this
+ * call writes.  The cache is a ring [ENGINE 8]: position p lives in row
+ * p % cap.  A sequence with more than one token in the call must keep its
+ * positions below cap (its later rows would overwrite positions its earlier
+ * tokens attend to); a sequence with one token may be at any position.
+ * cap <= 8192.
  * ws: qk_layer_workspace(cfg, tokens) bytes. */
 int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t tokens,
                   const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,

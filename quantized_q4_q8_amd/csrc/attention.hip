@@ -57,9 +57,11 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
     const int G = (int)(nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
+    if (p < 0) return;   // negative positions read nothing
+    const int64_t pe = min((int64_t)p, cap - 1);   // last ring row attended
     const int64_t r0 = c * ACH;
-    if (p < 0 || p >= cap || r0 > p) return;   // out-of-range positions read nothing
-    const int rows = (int)min((int64_t)ACH, (int64_t)p + 1 - r0);
+    if (r0 > pe) return;
+    const int rows = (int)min((int64_t)ACH, pe + 1 - r0);
     const double rscale = sqrt((double)HD);
 
     for (int i = tid; i < G * HD; i += 512)
@@ -169,8 +171,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
     const int64_t col = h * HD;
-    const bool valid = p >= 0 && p < cap;   // out-of-range position: zeros, no reads
-    const int used = valid ? p / ACH + 1 : 0;
+    const bool valid = p >= 0;   // negative position: zeros, no reads
+    const int used = valid ? (int)(min((int64_t)p, cap - 1) / ACH) + 1 : 0;
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
     const int pr = tid % PAIRS, sl = tid / PAIRS;
 
@@ -274,9 +276,9 @@ __global__ __launch_bounds__(512) void k_attn_flash(
             pi[i] = -1;
             if (i < nrun) {
                 const int p = pos[t0 + i0 + i];
-                if (p >= 0 && p < cap) {   // out-of-range positions attend to nothing
-                    pi[i] = p;
-                    kmax = max(kmax, p);
+                if (p >= 0) {   // negative positions attend to nothing
+                    pi[i] = (int)min((int64_t)p, cap - 1);   // last ring row attended
+                    kmax = max(kmax, pi[i]);
                 }
             }
         }

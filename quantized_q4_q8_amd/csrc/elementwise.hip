@@ -80,7 +80,8 @@ int launch_rmsnorm_q8(const float* x, const float* gamma, int64_t rows, int64_t 
 // (token, pair) and the result rounded once to fp32.
 // One workgroup per token; q heads then k heads are rotated in place, after
 // which (when caches are given) k and v rows are stored to the fp16 KV cache
-// at row pos of the token's sequence (TinyLLaMA-in-C++ guide, section 7).
+// at ring row pos % cap of the token's sequence (TinyLLaMA-in-C++ guide,
+// section 7; the ring buffer of the inference-engine article, section 8).
 __global__ __launch_bounds__(256) void k_rope_kv(float* __restrict__ base, int64_t tok_stride,
                                                  int64_t q_off, int64_t nq, int64_t k_off,
                                                  int64_t v_off, int64_t nkv, int64_t hd,
@@ -110,17 +111,17 @@ __global__ __launch_bounds__(256) void k_rope_kv(float* __restrict__ base, int64
         const double x1 = v.x, x2 = v.y;
         const float2 o = make_float2((float)(x1 * c - x2 * sn), (float)(x1 * sn + x2 * c));
         *reinterpret_cast<float2*>(xp) = o;
-        if (kc && hh >= nq && p >= 0 && p < cap) {
+        if (kc && hh >= nq && p >= 0) {
             const int64_t g = hh - nq;
-            const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + p) * hd + 2 * i;
+            const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + p % cap) * hd + 2 * i;
             kc[dst] = f2h(o.x);
             kc[dst + 1] = f2h(o.y);
         }
     }
-    if (vc && p >= 0 && p < cap) {
+    if (vc && p >= 0) {
         for (int64_t idx = threadIdx.x; idx < nkv * hd; idx += 256) {
             const int64_t g = idx / hd, d = idx % hd;
-            const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + p) * hd + d;
+            const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + p % cap) * hd + d;
             vc[dst] = f2h(row[v_off + g * hd + d]);
         }
     }
@@ -147,8 +148,8 @@ __global__ __launch_bounds__(256) void k_kv_append(const float* __restrict__ k,
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= tokens * nkv * hd) return;
     const int64_t d = i % hd, g = (i / hd) % nkv, t = i / (hd * nkv);
-    if (pos[t] < 0 || pos[t] >= cap) return;  // out-of-range rows are not written
-    const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + pos[t]) * hd + d;
+    if (pos[t] < 0) return;  // negative positions are not written
+    const int64_t dst = (((int64_t)seq[t] * nkv + g) * cap + pos[t] % cap) * hd + d;
     kc[dst] = f2h(k[i]);
     vc[dst] = f2h(v[i]);
 }

@@ -421,11 +421,11 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
                     if (row0 < a.q_rows) {
                         a.q_out[ocol * a.q_rows + row0] = (float)(x1 * c - x2 * sn);
                         a.q_out[ocol * a.q_rows + row0 + 1] = (float)(x1 * sn + x2 * c);
-                    } else if (p >= 0 && p < a.cap) {
+                    } else if (p >= 0) {   // ring row p % cap
                         const bool is_k = row0 < a.q_rows + a.kv_rows;
                         const int64_t rr = row0 - a.q_rows - (is_k ? 0 : a.kv_rows);
                         const int64_t gh = rr / a.hd, d = rr % a.hd;
-                        const int64_t dst = (((int64_t)a.seq[ocol] * a.n_kv + gh) * a.cap + p) * a.hd + d;
+                        const int64_t dst = (((int64_t)a.seq[ocol] * a.n_kv + gh) * a.cap + p % a.cap) * a.hd + d;
                         uint16_t* cache = is_k ? a.kc : a.vc;
                         const float o1 = (float)(is_k ? x1 * c - x2 * sn : x1);
                         const float o2 = (float)(is_k ? x1 * sn + x2 * c : x2);

@@ -92,6 +92,48 @@ def test_layer_ragged_sequences(gpu_lib, tokens):
     assert_same_fp32(host(xg), ref)
 
 
+@pytest.mark.parametrize("seqs", [1, 3, 12])
+def test_layer_decode_through_ring_wrap(gpu_lib, seqs):
+    """Decode past the cache capacity (the cache is a ring, position p in row
+    p % cap): each sequence is prefilled with 12 tokens into a 20-row cache,
+    then all sequences decode 24 steps together, one token each per call, each
+    side feeding back its own output.  With 12 sequences the calls take the
+    many-token path (MFMA matmuls, tiled attention)."""
+    qk = gpu_lib
+    g = W.Geometry(256, 8, 2, 32, 160)
+    cap, P, steps = 20, 12, 24
+    say(f"layer_forward ring wrap seqs={seqs} cap={cap}")
+    wf = W.layer_weights_f32(41, 2, g)
+    wl = oracle_layer(wf)
+    lw = layer_to_device(wf)
+    cfg = qk.layer_cfg(**g.cfg(cap))
+    kshape = (seqs, g.n_kv_heads, cap, g.head_dim)
+    kc, vc = np.zeros(kshape, np.uint16), np.zeros(kshape, np.uint16)
+    kcg, vcg = dev(kc), dev(vc)
+    o_in, g_in = [], []
+    for s in range(seqs):
+        x = synth.normal(41, 10 + s, (P, g.hidden))
+        pos, seq = np.arange(P, dtype=np.int32), np.full(P, s, np.int32)
+        ref = oracle.layer_forward(wl, g.cfg(cap), x, pos, seq, kc, vc)
+        xg = dev(x)
+        qk.layer_forward(lw, cfg, xg, dev(pos), dev(seq), kcg, vcg)
+        assert_same_fp32(host(xg), ref)
+        o_in.append(ref[-1])
+        g_in.append(host(xg)[-1])
+    o_in, g_in = np.stack(o_in), np.stack(g_in)
+    seq = np.arange(seqs, dtype=np.int32)
+    for step in range(steps):
+        pos = np.full(seqs, P + step, np.int32)
+        o_out = oracle.layer_forward(wl, g.cfg(cap), o_in, pos, seq, kc, vc)
+        xs = dev(g_in)
+        qk.layer_forward(lw, cfg, xs, dev(pos), dev(seq), kcg, vcg)
+        g_out = host(xs)
+        assert rel_err(g_out, o_out) < LAYER_TOL, f"decode step {step} (position {P + step})"
+        assert_same_fp32(g_out, o_out)
+        o_in, g_in = o_out, g_out
+    assert np.mean(host(kcg, np.uint16) == kc) > 0.999
+
+
 def test_layer_decode_equals_prefill_last_row(gpu_lib):
     qk = gpu_lib
     g = W.LAYER_SMALL["geometry"]

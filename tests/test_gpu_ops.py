@@ -216,6 +216,13 @@ def test_kv_append_bit_exact(gpu_lib):
     oracle.kv_append(k, v, pos, seq, kc, vc)
     assert np.array_equal(host(kcg, np.uint16), kc)
     assert np.array_equal(host(vcg, np.uint16), vc)
+    # past cap, one token per sequence: ring rows pos % cap
+    pos = np.array([40, 1000, 79], np.int32)
+    seq = np.array([0, 1, 2], np.int32)
+    qk.qk_kv_append(dev(k[:3]), dev(v[:3]), dev(pos), dev(seq), kcg, vcg)
+    oracle.kv_append(k[:3], v[:3], pos, seq, kc, vc)
+    assert np.array_equal(host(kcg, np.uint16), kc)
+    assert np.array_equal(host(vcg, np.uint16), vc)
 
 
 def test_embed_and_argmax(gpu_lib):
@@ -256,6 +263,11 @@ ATT_CASES = [
     (40, 32, 4, 64, 300, 3, "runs"),
     (37, 16, 1, 32, 130, 2, "random"),
     (12, 32, 4, 64, 2176, 1, "long"),
+    # past cap the cache is a ring: one token per sequence, any position
+    (3, 32, 4, 64, 4096, 3, "ring"),
+    (2, 32, 4, 64, 8192, 2, "ring"),
+    (3, 8, 2, 64, 100, 3, "ring"),
+    (12, 16, 2, 64, 100, 12, "ring"),     # many tokens: the tiled pass
 ]
 
 
@@ -278,6 +290,9 @@ def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
         pos = np.array([90 * (t // 14) + t % 14 + 3 for t in range(tokens)], np.int32)
     elif recipe == "long":
         pos = (2100 + np.arange(tokens)).astype(np.int32)
+    elif recipe == "ring":
+        pos = np.array([cap - 1, cap, 2 * cap + 37, 5 * cap + 3] * 3, np.int32)[:tokens] + \
+            (synth.randint(111, 5, tokens, 7)).astype(np.int32)
     else:
         pos = (synth.randint(111, 4, tokens, cap)).astype(np.int32)
     if recipe != "runs":
