@@ -38,9 +38,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="decode", choices=["decode", "matmul", "prefill", "moe", "sample"],
-                    help="decode (the headline line); the others measure the standalone matmul, "
-                         "prefill, MoE and sampler workloads")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "longctx", "matmul", "prefill", "moe", "sample"],
+                    help="decode (the headline line); the others measure decode past an "
+                         "8192-row ring cache and the standalone matmul, prefill, MoE and "
+                         "sampler workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -133,13 +135,14 @@ def decode_bytes_per_token(spec) -> float:
     H, F = g.hidden, g.ffn_padded
     q4 = 9 / 16  # bytes per Q4_0 weight
     lin = L * (g.n_qkv * H + H * g.n_q_heads * g.head_dim + 2 * F * H + H * F) + V * H
-    mean_ctx = spec["context"] + (spec["steps"] - 1) / 2 + 1       # rows read per layer
+    # cache rows read per layer, averaged over the steps (the ring holds cap)
+    mean_ctx = sum(min(spec["context"] + j + 1, spec["cap"]) for j in range(spec["steps"])) / spec["steps"]
     kv = L * 2 * g.n_kv_heads * g.head_dim * 2 * mean_ctx
     norms = (2 * L + 1) * H * 4
     return lin * q4 + kv + norms + H * 4
 
 
-def run_decode(args):
+def run_decode(args, long_context: bool = False):
     import numpy as np
     import torch
 
@@ -147,7 +150,7 @@ def run_decode(args):
     from synth import normal
     from synth import workloads as W
 
-    spec = W.DECODE
+    spec = W.DECODE_LONG if long_context else W.DECODE
     g, L = spec["geometry"], spec["layers"]
     steps_per_run = max(1, min(args.decode_tokens, spec["steps"]))
     want_cpu = not args.no_cpu_baseline
@@ -236,8 +239,16 @@ def run_decode(args):
     del cal_src, cal_dst
 
     step_bytes = decode_bytes_per_token(spec)
+    c0, c1 = spec["context"], spec["context"] + steps_per_run - 1
+    if long_context:
+        metric = "decode tokens/s at TinyLLaMA-1.1B Q4_0 shape, 8192-row ring KV cache"
+        workload = (f"tinyllama-1.1b-shape greedy decode, 22 layers, positions {c0}->{c1} "
+                    f"through an {spec['cap']}-row ring cache (every step attends {spec['cap']} positions)")
+    else:
+        metric = "decode tokens/s at TinyLLaMA-1.1B Q4_0 shape"
+        workload = f"tinyllama-1.1b-shape greedy decode, 22 layers, context {c0}->{c1}"
     out = {
-        "metric": "decode tokens/s at TinyLLaMA-1.1B Q4_0 shape",
+        "metric": metric,
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -249,7 +260,7 @@ def run_decode(args):
         "vs_baseline": None,
         "dtype": "q4_0 x q8_0 (int32 block dots, fp64 accumulate, fp32 activations)",
         "data": "synthetic: seeded N(0,0.02) Q4_0 weights, N(0,1) fp16 KV prefill",
-        "config": {"workload": "tinyllama-1.1b-shape greedy decode, 22 layers, context 2048->2175",
+        "config": {"workload": workload, "kv_cap": spec["cap"],
                    "tokens_per_step": steps_per_run, "batch": 1, "layers": L,
                    "hidden": g.hidden, "heads": [g.n_q_heads, g.n_kv_heads, g.head_dim],
                    "ffn": g.ffn, "vocab": spec["vocab"], "kv_cache": "fp16",
@@ -298,8 +309,9 @@ def cpu_decode_baseline(spec, host, first, budget_s: float):
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     log(f"oracle: {n} tokens in {t_total:.1f}s on {threads} threads")
     return {"value": round(n / t_total, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} greedy decode tokens (positions 2048..{2047 + n}) of the same "
-                      f"22-layer workload, oracle in fp64/exact-int C++ with OpenMP"}
+            "sample": f"{n} greedy decode tokens (positions {spec['context']}.."
+                      f"{spec['context'] + n - 1}) of the same 22-layer workload, oracle in "
+                      f"fp64/exact-int C++ with OpenMP"}
 
 
 def graph_time_us(fn, launches: int, rounds: int) -> float:
@@ -601,7 +613,7 @@ def main():
         sys.exit(1)
     import quantized_q4_q8_amd as qk
     qk.load()
-    {"decode": run_decode, "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
+    {"decode": run_decode, "longctx": lambda a: run_decode(a, long_context=True), "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -130,6 +130,10 @@ MATMUL = dict(seed=1, shapes=[(5632, 2048), (2048, 5632)], batches=[1, 8])
 TINYLLAMA = Geometry(2048, 32, 4, 64, 5632)
 DECODE = dict(seed=2, geometry=TINYLLAMA, layers=22, vocab=32000, context=2048, steps=128,
               cap=2176)
+# Long context: the same decode with an 8192-row ring cache filled to the
+# brim; positions 8192..8319 wrap, so every step attends to 8192 positions.
+DECODE_LONG = dict(seed=5, geometry=TINYLLAMA, layers=22, vocab=32000, context=8192, steps=128,
+                   cap=8192)
 # C4: TinyLLaMA-1.1B-shaped prefill: batch 4 x 512 uniform token ids, causal, full logits.
 PREFILL = dict(seed=3, geometry=TINYLLAMA, layers=22, vocab=32000, batch=4, prompt=512, cap=512)
 # C5: MoE layer, hidden 6144, 256 experts of width 2048, sigmoid top-8, 64 tokens.
