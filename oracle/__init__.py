@@ -65,6 +65,10 @@ _SIGS = {
     "oracle_moe_expert_ffn": ([_P, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "oracle_moe_route_and_apply": ([_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P, _I64, _P,
                                     _P, _P], ctypes.c_int),
+    "oracle_quantize_rowq": ([_I32, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "oracle_qmatmul_rowq_q8_0": ([_I32, _P, _P, _I64, _I64, _P, _P, _I64, _P], ctypes.c_int),
+    "oracle_moe_route_and_apply_rowq": ([_I32, _P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P,
+                                         _I64, _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -161,6 +165,31 @@ def qmatmul(wq, wd, xq, xd) -> np.ndarray:
     y = np.empty((m, n), np.float32)
     _check(lib().oracle_qmatmul_q4_0_q8_0(_p(wq), _p(wd), n, k, _p(xq), _p(xd), m, _p(y)),
            "qmatmul")
+    return y
+
+
+def quantize_rowq(w, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Row-scaled int4 (bits 4) or int2 (bits 2) of an fp32 [n][k] matrix ->
+    (codes uint8 [n][k * bits / 8], scales fp32 [n])."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    wq = np.empty((n, k * bits // 8), np.uint8)
+    wr = np.empty(n, np.float32)
+    _check(lib().oracle_quantize_rowq(bits, _p(w), n, k, _p(wq), _p(wr)), "quantize_rowq")
+    return wq, wr
+
+
+def qmatmul_rowq(wq, wr, xq, xd, bits: int) -> np.ndarray:
+    """y [m][n] = row-scaled int4/int2 W [n][k] times Q8_0 x [m][k] (fp32 out)."""
+    wq = _c(wq, np.uint8)
+    wr = _c(wr, np.float32)
+    n, k = wq.shape[0], wq.shape[1] * 8 // bits
+    xq = _c(xq, np.int8).reshape(-1, k)
+    xd = _c(xd, np.uint16).reshape(-1, k // 32)
+    m = xq.shape[0]
+    y = np.empty((m, n), np.float32)
+    _check(lib().oracle_qmatmul_rowq_q8_0(bits, _p(wq), _p(wr), n, k, _p(xq), _p(xd), m, _p(y)),
+           "qmatmul_rowq")
     return y
 
 
@@ -318,4 +347,22 @@ def moe_route_and_apply(x, w_router, top_k: int, gu_q, gu_d, dn_q, dn_d):
         _p(x), t, hidden, _p(w_router), e, top_k, _p(_c(gu_q, np.uint8)), _p(_c(gu_d, np.uint16)),
         _p(_c(dn_q, np.uint8)), _p(_c(dn_d, np.uint16)), ffn, _p(out), _p(idx), _p(wts)),
         "moe_route_and_apply")
+    return out, idx, wts
+
+
+def moe_route_and_apply_rowq(x, w_router, top_k: int, gu_q, gu_r, dn_q, dn_r, bits: int):
+    """Row-scaled experts stacked: gu_q [E][2F][H * bits / 8], gu_r [E][2F] fp32,
+    dn_q [E][H][F * bits / 8], dn_r [E][H].  Returns (out, sel_idx, sel_w)."""
+    x = _c(x, np.float32)
+    w_router = _c(w_router, np.float32)
+    t, hidden = x.shape
+    e = w_router.shape[1]
+    ffn = gu_q.shape[1] // 2
+    out = np.empty_like(x)
+    idx = np.empty((t, top_k), np.int32)
+    wts = np.empty((t, top_k), np.float32)
+    _check(lib().oracle_moe_route_and_apply_rowq(
+        bits, _p(x), t, hidden, _p(w_router), e, top_k, _p(_c(gu_q, np.uint8)), _p(_c(gu_r, np.float32)),
+        _p(_c(dn_q, np.uint8)), _p(_c(dn_r, np.float32)), ffn, _p(out), _p(idx), _p(wts)),
+        "moe_route_and_apply_rowq")
     return out, idx, wts

@@ -30,7 +30,8 @@
  *  [COLIBRI]  kerneldigest.dev, "Colibri: running 744B MoE models on consumer
  *             hardware by streaming experts": "System architecture" and the
  *             token-flow figure (sigmoid router, int8 activations, expert
- *             kernels, combine).
+ *             kernels, combine); the model-conversion flow and the layer
+ *             table (int4 container with per-row scales, int4/int2 packing).
  *
  * Parity pins: every function here is checked by the CPU test suite against
  * closed forms, invariants, numpy's IEEE binary16 conversion or fp64 brute
@@ -187,6 +188,76 @@ void qmatmul(const uint8_t* w_q, const uint16_t* w_d, int64_t n, int64_t k,
                 acc += h2d(w_d[r * nb + b]) * h2d(x_d[t * nb + b]) * (double)isum;
             }
             y[t * n + r] = (float)acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-scaled int4 / int2 weights [COLIBRI "System architecture" and the
+// model-conversion flow: the engine's int4 container carries one scale per
+// row, and its integer kernels pack int4 and int2 codes].  For bits b:
+//   delta = max|w_row| / (2^(b-1) - 1) in fp32 (/7 for int4, as for Q4_0;
+//   /1 for int2), q = round-half-away-from-zero(w / delta) clamped to
+//   [-2^(b-1), 2^(b-1) - 1], stored as q + 2^(b-1); delta stays fp32.
+// A row of zeros stores delta 0 and q = 0.  Per 32-element group:
+//   int4: 16 bytes, byte j holds element j (low nibble) and j + 16 (high);
+//   int2: 8 bytes, byte j holds elements j, j + 8, j + 16, j + 24 in bits
+//         0-1, 2-3, 4-5, 6-7.
+// ---------------------------------------------------------------------------
+void rowq_quantize_row(int bits, const float* w, int64_t k, uint8_t* packed, float* d) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < k; ++i) amax = std::max(amax, std::fabs(w[i]));
+    const int hi = (1 << (bits - 1)) - 1, lo = -(1 << (bits - 1));
+    const float delta = amax / (float)hi;
+    const int64_t group_bytes = bits * QBLK / 8;
+    std::memset(packed, 0, (size_t)(k / QBLK * group_bytes));
+    for (int64_t i = 0; i < k; ++i) {
+        int q = 0;
+        if (delta != 0.0f) {
+            float v = std::roundf(w[i] / delta);
+            v = std::min((float)hi, std::max((float)lo, v));
+            q = (int)v;
+        }
+        const uint8_t c = (uint8_t)(q - lo);
+        const int64_t g = i / QBLK;
+        const int j = (int)(i % QBLK);
+        if (bits == 4)
+            packed[g * group_bytes + (j & 15)] |= (uint8_t)(c << (j < 16 ? 0 : 4));
+        else
+            packed[g * group_bytes + (j & 7)] |= (uint8_t)(c << (2 * (j / 8)));
+    }
+    *d = delta;
+}
+
+// Signed code of element i of a row-scaled row.
+inline int rowq_code(int bits, const uint8_t* row_q, int64_t i) {
+    const int64_t g = i / QBLK;
+    const int j = (int)(i % QBLK);
+    if (bits == 4) {
+        const uint8_t byte = row_q[g * 16 + (j & 15)];
+        return ((j < 16) ? (byte & 0x0F) : (byte >> 4)) - 8;
+    }
+    const uint8_t byte = row_q[g * 8 + (j & 7)];
+    return ((byte >> (2 * (j / 8))) & 3) - 2;
+}
+
+// y[t][r] = delta_r * sum_b dx[t][b] * isum[t][r][b], isum the exact integer
+// dot of block b, in double, rounded to fp32 once.
+void rowq_matmul(int bits, const uint8_t* w_q, const float* w_r, int64_t n, int64_t k,
+                 const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y) {
+    const int64_t nb = k / QBLK, row_bytes = k * bits / 8;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < m; ++t) {
+        for (int64_t r = 0; r < n; ++r) {
+            const uint8_t* rq = w_q + r * row_bytes;
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                int32_t isum = 0;
+                for (int j = 0; j < QBLK; ++j)
+                    isum += rowq_code(bits, rq, b * QBLK + j) * (int32_t)x_q[t * k + b * QBLK + j];
+                acc += h2d(x_d[t * nb + b]) * (double)isum;
+            }
+            y[t * n + r] = (float)((double)w_r[r] * acc);
         }
     }
 }
@@ -381,6 +452,20 @@ int oracle_qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_t n,
                              const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y) {
     if (k <= 0 || k % QBLK || n < 0 || m < 0) return E_SHAPE;
     qmatmul(w_q, w_d, n, k, x_q, x_d, m, y);
+    return OK;
+}
+
+int oracle_quantize_rowq(int32_t bits, const float* w, int64_t n, int64_t k, uint8_t* w_q, float* w_r) {
+    if ((bits != 4 && bits != 2) || k <= 0 || k % QBLK || n < 0) return E_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) rowq_quantize_row(bits, w + r * k, k, w_q + r * (k * bits / 8), w_r + r);
+    return OK;
+}
+
+int oracle_qmatmul_rowq_q8_0(int32_t bits, const uint8_t* w_q, const float* w_r, int64_t n, int64_t k,
+                             const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y) {
+    if ((bits != 4 && bits != 2) || k <= 0 || k % QBLK || n < 0 || m < 0) return E_SHAPE;
+    rowq_matmul(bits, w_q, w_r, n, k, x_q, x_d, m, y);
     return OK;
 }
 
@@ -631,6 +716,45 @@ int oracle_moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden, c
             for (int32_t kk = 0; kk < top_k; ++kk)
                 acc += (double)sel_w[t * top_k + kk] * (double)ys[(size_t)((t * top_k + kk) * hidden + i)];
             out[t * hidden + i] = (float)acc;
+        }
+    return OK;
+}
+
+// The routed MoE layer with row-scaled int4 or int2 experts: routing and
+// combine as above; each expert's FFN with the row-scaled matmul.  Experts
+// are stacked: gu_q [E][2F][hidden * bits / 8], gu_r [E][2F] (fp32),
+// dn_q [E][hidden][F * bits / 8], dn_r [E][hidden].
+int oracle_moe_route_and_apply_rowq(int32_t bits, const float* x, int64_t tokens, int64_t hidden,
+                                    const float* w_router, int64_t n_experts, int32_t top_k,
+                                    const uint8_t* gu_q, const float* gu_r, const uint8_t* dn_q,
+                                    const float* dn_r, int64_t ffn, float* out, int32_t* sel_idx,
+                                    float* sel_w) {
+    if (bits != 4 && bits != 2) return E_SHAPE;
+    int rc = oracle_moe_route(x, tokens, hidden, w_router, n_experts, top_k, sel_idx, sel_w, nullptr);
+    if (rc) return rc;
+    if (hidden % QBLK || ffn % QBLK) return E_SHAPE;
+    const int64_t F = ffn, H = hidden;
+    std::vector<float> ys((size_t)(tokens * top_k * H));
+    std::vector<int8_t> xq((size_t)std::max(H, F));
+    std::vector<uint16_t> xd((size_t)(std::max(H, F) / QBLK));
+    std::vector<float> gu((size_t)(2 * F)), h((size_t)F);
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int32_t kk = 0; kk < top_k; ++kk) {
+            const int64_t e = sel_idx[t * top_k + kk];
+            quantize_q8(x + t * H, 1, H, xq.data(), xd.data());
+            rowq_matmul(bits, gu_q + e * 2 * F * (H * bits / 8), gu_r + e * 2 * F, 2 * F, H, xq.data(),
+                        xd.data(), 1, gu.data());
+            swiglu(gu.data(), gu.data() + F, F, h.data());
+            quantize_q8(h.data(), 1, F, xq.data(), xd.data());
+            rowq_matmul(bits, dn_q + e * H * (F * bits / 8), dn_r + e * H, H, F, xq.data(), xd.data(), 1,
+                        &ys[(size_t)((t * top_k + kk) * H)]);
+        }
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t i = 0; i < H; ++i) {
+            double acc = 0.0;
+            for (int32_t kk = 0; kk < top_k; ++kk)
+                acc += (double)sel_w[t * top_k + kk] * (double)ys[(size_t)((t * top_k + kk) * H + i)];
+            out[t * H + i] = (float)acc;
         }
     return OK;
 }

@@ -155,6 +155,85 @@ def test_q4_0_error_bound_random():
 
 
 # ---------------------------------------------------------------------------
+# row-scaled int4 / int2 (COLIBRI: int4 container with per-row scales,
+# int4/int2 packing)
+# ---------------------------------------------------------------------------
+def unpack_rowq(wq, bits):
+    """Signed codes in element order from the documented packing (numpy)."""
+    n, nbytes = wq.shape
+    if bits == 4:
+        return unpack_q4(wq) - 8
+    g = wq.reshape(n, nbytes // 8, 8).astype(np.int32)
+    parts = [(g >> (2 * s)) & 3 for s in range(4)]        # elements j + 8 s
+    return np.concatenate(parts, axis=-1).reshape(n, nbytes * 4) - 2
+
+
+def test_rowq_unit_scale_codes_and_layout():
+    """max|w| = 7 (int4) or 1 (int2) gives delta 1 exactly, so the codes are
+    the weights rounded half away from zero; the bytes follow the documented
+    order (worked by hand)."""
+    w4 = np.array([[-7, -2.5, 2.5, 0.5, -0.5, 7, 1.49, 3.51] * 4], np.float32)
+    q4, r4 = oracle.quantize_rowq(w4, 4)
+    assert r4.tolist() == [1.0]
+    assert q4[0, :8].tolist() == [0x11, 0x55, 0xBB, 0x99, 0x77, 0xFF, 0x99, 0xCC]
+    # nibble of element i = i % 16  ->  byte j = j | j << 4
+    w4b = np.array([[(i % 16) - 8 for i in range(32)]], np.float32)
+    w4b[0, 0] = w4b[0, 16] = -7.0                            # keep max|w| = 7 (code -8 never made)
+    q4b, _ = oracle.quantize_rowq(w4b, 4)
+    assert q4b[0].tolist() == [0x11] + [j | (j << 4) for j in range(1, 16)]
+    w2 = np.array([[-1, 0, 1, 0.5, -0.5, 0.49, -0.49, 0.2] * 4], np.float32)
+    q2, r2 = oracle.quantize_rowq(w2, 2)
+    assert r2.tolist() == [1.0]
+    assert q2[0].tolist() == [0x55, 0xAA, 0xFF, 0xFF, 0x55, 0xAA, 0xAA, 0xAA]
+    # stored code of element i = 1 + (i // 8) % 3  ->  byte j = 1 | 2 << 2 | 3 << 4 | 1 << 6
+    w2b = np.array([[((i // 8) % 3) - 1 for i in range(32)]], np.float32)
+    q2b, _ = oracle.quantize_rowq(w2b, 2)
+    assert q2b[0].tolist() == [0x79] * 8
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_rowq_zero_row_extremes_and_error_bound(bits):
+    hi = 7 if bits == 4 else 1
+    w = synth.normal(35, bits, (64, 256), 0.02)
+    w[3] = 0.0
+    wq, wr = oracle.quantize_rowq(w, bits)
+    q = unpack_rowq(wq, bits)
+    assert wr[3] == 0 and np.all(q[3] == 0)
+    assert q.min() >= -hi and q.max() <= hi                 # -8 / -2 never made
+    amax = np.abs(w).max(1)
+    delta = (amax / np.float32(hi)).astype(np.float32)
+    assert np.array_equal(wr, delta)
+    arg = np.abs(w).argmax(1)
+    assert np.all(np.abs(q[np.arange(64), arg])[amax > 0] == hi)
+    recon = wr.astype(np.float64)[:, None] * q
+    assert np.all(np.abs(w - recon) <= wr.astype(np.float64)[:, None] / 2 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_qmatmul_rowq_equals_fp64_dequantized_bruteforce(bits):
+    """y = delta_r * sum_b dx_b * isum_b equals the fp64 product of the
+    dequantized matrices (to fp64 rounding), with exactly representable
+    weights (w = 2^-6 q) and random ones."""
+    hi = 7 if bits == 4 else 1
+    n, k, m = 9, 96, 3
+    codes = synth.randint(36, bits, (n, k), 2 * hi + 1).astype(np.int32) - hi
+    codes[:, 5] = hi                                         # max|w| = hi * delta
+    w_exact = (codes * 2.0 ** -6).astype(np.float32)
+    x = synth.normal(36, 10 + bits, (m, k))
+    xq, xd = oracle.quantize_q8_0(x)
+    xdeq = oracle.f16_to_f32(xd).astype(np.float64).repeat(32, 1) * xq
+    for w in (w_exact, synth.normal(36, 20 + bits, (n, k), 0.02)):
+        wq, wr = oracle.quantize_rowq(w, bits)
+        y = oracle.qmatmul_rowq(wq, wr, xq, xd, bits)
+        wdeq = wr.astype(np.float64)[:, None] * unpack_rowq(wq, bits)
+        assert np.allclose(y, xdeq @ wdeq.T, rtol=1e-6, atol=1e-9)
+    assert np.array_equal(unpack_rowq(oracle.quantize_rowq(w_exact, bits)[0], bits), codes)
+    # zero weights give zero exactly
+    assert np.all(oracle.qmatmul_rowq(*oracle.quantize_rowq(np.zeros((4, k), np.float32), bits),
+                                      xq, xd, bits) == 0)
+
+
+# ---------------------------------------------------------------------------
 # block dots and the quantized matmul
 # ---------------------------------------------------------------------------
 def test_block_dot_extremes_and_one_hot():
@@ -624,6 +703,44 @@ def test_moe_identical_experts_give_single_expert_output():
     for t in range(T):
         single = oracle.moe_expert_ffn(x[t], gq[0], gd[0], dq[0], dd[0])
         assert np.allclose(out[t], single, rtol=1e-6, atol=1e-8)
+
+
+def _experts_rowq(seed, E, H, F, bits):
+    gq, gr, dq, dr = [], [], [], []
+    for e in range(E):
+        gu, dn = W.expert_weights_f32(seed, e, H, F)
+        a, b = oracle.quantize_rowq(gu, bits)
+        c, d = oracle.quantize_rowq(dn, bits)
+        gq.append(a), gr.append(b), dq.append(c), dr.append(d)
+    return np.stack(gq), np.stack(gr), np.stack(dq), np.stack(dr)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_moe_rowq_sparse_equals_dense_bruteforce(bits):
+    """Row-scaled experts: the routed layer equals evaluating every expert on
+    every token (Q8_0, row-scaled matmul, SwiGLU, Q8_0, row-scaled matmul),
+    then selecting and combining in fp64."""
+    T, H, E, F, k = 4, 64, 8, 32, 3
+    x = synth.normal(37, 1, (T, H))
+    wrt = synth.normal(37, 2, (H, E), 0.3)
+    gq, gr, dq, dr = _experts_rowq(37, E, H, F, bits)
+    out, idx, w = oracle.moe_route_and_apply_rowq(x, wrt, k, gq, gr, dq, dr, bits)
+
+    def expert(t, e):
+        xq, xd = oracle.quantize_q8_0(x[t:t + 1])
+        gu = oracle.qmatmul_rowq(gq[e], gr[e], xq, xd, bits)[0]
+        h = oracle.swiglu(gu[:F], gu[F:])
+        hq, hd = oracle.quantize_q8_0(h[None])
+        return oracle.qmatmul_rowq(dq[e], dr[e], hq, hd, bits)[0]
+
+    dense = np.stack([[expert(t, e) for e in range(E)] for t in range(T)])
+    r = x.astype(np.float64) @ wrt.astype(np.float64)
+    sel = np.argsort(-r, axis=1, kind="stable")[:, :k]
+    s = 1 / (1 + np.exp(-np.take_along_axis(r, sel, 1)))
+    ww = s / s.sum(1, keepdims=True)
+    ref = np.einsum("tk,tkh->th", ww, np.take_along_axis(dense, sel[:, :, None], 1).astype(np.float64))
+    assert np.array_equal(idx, sel)
+    assert np.allclose(out, ref, rtol=1e-5, atol=1e-7)
 
 
 def test_expert_ffn_fp64_bruteforce():
