@@ -13,7 +13,9 @@
  *  [ENGINE]   kenji.blog, "No Python needed: an AI inference engine in C++
  *             only": 6 GEMM, 7.1 backend interface, 8 attention and KV cache.
  *  [COLIBRI]  kerneldigest.dev, "Colibri: running 744B MoE models on consumer
- *             hardware by streaming experts": System architecture, token flow.
+ *             hardware by streaming experts": System architecture, token flow,
+ *             model-conversion flow and layer table (per-row int4 container,
+ *             int4/int2 packing).
  *
  * Conventions (all entry points):
  *  - Every pointer argument is a DEVICE pointer owned by the caller, unless
@@ -300,6 +302,44 @@ int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden, const fl
 
 size_t qk_moe_workspace(int64_t tokens, int64_t hidden, int64_t n_experts, int32_t top_k,
                         int64_t ffn);
+
+/* ---------------------------------------------------------------------- */
+/* Row-scaled int4 / int2 weights                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Row-scaled quantization [COLIBRI: the engine's int4 container with one
+ * scale per row (model-conversion flow); int4/int2 packing (layer table)].
+ * bits 4 or 2.  Per row: delta = max|w| / (2^(bits-1) - 1) in fp32 (/7 or
+ * /1), code = round-half-away-from-zero(w / delta) clamped to
+ * [-2^(bits-1), 2^(bits-1) - 1], stored as code + 2^(bits-1); a zero row
+ * stores delta 0 and code 0.  Per 32-element group of a row, int4 takes 16
+ * bytes (byte j: element j in the low nibble, j + 16 in the high one, as
+ * Q4_0) and int2 takes 8 bytes (byte j: elements j, j + 8, j + 16, j + 24 in
+ * bits 0-1, 2-3, 4-5, 6-7).  w fp32 [n][k] (16-byte aligned), w_q uint8
+ * [n][k * bits / 8] (16-byte aligned), w_r fp32 [n]; device memory; k % 32
+ * == 0.  QK_EINVAL for other bits. */
+int qk_quantize_rowq(int32_t bits, const float* w, int64_t n, int64_t k, uint8_t* w_q, float* w_r,
+                     void* stream);
+
+/* y[t][r] = w_r[r] * sum_b dx[t][b] * isum[t][r][b] with isum the exact int32
+ * dot of row r's block b codes with x_q (fp64 accumulation, one rounding to
+ * fp32).  Same layouts as qk_quantize_rowq; x_q, x_d as qmatmul_q4_0_q8_0.
+ * Any m (passes of up to 8 columns); k up to 58176. */
+int qk_qmatmul_rowq_q8_0(int32_t bits, const uint8_t* w_q, const float* w_r, int64_t n, int64_t k,
+                         const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y,
+                         void* stream);
+
+/* moe_route_and_apply with row-scaled int4 (bits 4) or int2 (bits 2) experts:
+ * gate_up_q [E][2 ffn][hidden * bits / 8], gate_up_r fp32 [E][2 ffn], down_q
+ * [E][hidden][ffn * bits / 8], down_r fp32 [E][hidden].  Routing, SwiGLU,
+ * Q8_0 of the expert inputs and the combine are those of
+ * moe_route_and_apply; ws: qk_moe_workspace() bytes. */
+int qk_moe_route_and_apply_rowq(int32_t bits, const float* x, int64_t tokens, int64_t hidden,
+                                const float* w_router, int64_t n_experts, int32_t top_k,
+                                const uint8_t* gate_up_q, const float* gate_up_r,
+                                const uint8_t* down_q, const float* down_r, int64_t ffn, float* y,
+                                int32_t* sel_idx, float* sel_w, void* ws, size_t ws_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

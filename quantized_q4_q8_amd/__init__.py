@@ -70,6 +70,10 @@ _SIGS = {
     "moe_route_and_apply": ([_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
                              _SZ, _P], ctypes.c_int),
     "qk_moe_workspace": ([_I64, _I64, _I64, _I32, _I64], _SZ),
+    "qk_quantize_rowq": ([_I32, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "qk_qmatmul_rowq_q8_0": ([_I32, _P, _P, _I64, _I64, _P, _P, _I64, _P, _P], ctypes.c_int),
+    "qk_moe_route_and_apply_rowq": ([_I32, _P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P, _I64, _P,
+                                     _P, _P, _P, _SZ, _P], ctypes.c_int),
     "qk_lm_head": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "qk_lm_head_workspace": ([_I64, _I64, _I64], _SZ),
     "qk_ffn_up": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
@@ -194,6 +198,28 @@ def qmatmul_q4_0_q8_0(w_q, w_d, x_q, x_d, out=None):
     _check(load().qmatmul_q4_0_q8_0(_dev(w_q, torch.uint8, "w_q"), _dev16(w_d, "w_d"), n,
                                     k, _dev(x_q, torch.int8, "x_q"), _dev16(x_d, "x_d"), m,
                                     _dev(y, torch.float32, "y"), _stream()), "qmatmul_q4_0_q8_0")
+    return y
+
+
+def qk_quantize_rowq(w: torch.Tensor, bits: int, out_q=None, out_r=None):
+    """Row-scaled int4 (bits 4) or int2 (bits 2) of fp32 w [n][k] ->
+    (uint8 codes [n][k * bits / 8], fp32 scales [n])."""
+    n, k = w.shape
+    q = _out(out_q, (n, k * bits // 8), torch.uint8, w)
+    r = _out(out_r, (n,), torch.float32, w)
+    _check(load().qk_quantize_rowq(bits, _dev(w, torch.float32, "w"), n, k, _dev(q, torch.uint8, "w_q"),
+                                   _dev(r, torch.float32, "w_r"), _stream()), "qk_quantize_rowq")
+    return q, r
+
+
+def qk_qmatmul_rowq_q8_0(w_q, w_r, x_q, x_d, bits: int, out=None):
+    """y [m][n] = row-scaled int4/int2 W [n][k] times Q8_0 x [m][k]."""
+    n, k = w_q.shape[0], w_q.shape[1] * 8 // bits
+    m = x_q.numel() // k
+    y = _out(out, (m, n), torch.float32, x_q)
+    _check(load().qk_qmatmul_rowq_q8_0(bits, _dev(w_q, torch.uint8, "w_q"), _dev(w_r, torch.float32, "w_r"),
+                                       n, k, _dev(x_q, torch.int8, "x_q"), _dev16(x_d, "x_d"), m,
+                                       _dev(y, torch.float32, "y"), _stream()), "qk_qmatmul_rowq_q8_0")
     return y
 
 
@@ -405,4 +431,26 @@ def moe_route_and_apply(x, w_router, top_k: int, gate_up_q, gate_up_d, down_q, d
         _dev(down_q, torch.uint8, "down_q"), _dev16(down_d, "down_d"), ffn,
         _dev(y, torch.float32, "y"), _dev(si, torch.int32, "sel_idx"), _dev(sw, torch.float32, "sel_w"),
         wsb.data_ptr(), need, _stream()), "moe_route_and_apply")
+    return y, si, sw
+
+
+def qk_moe_route_and_apply_rowq(x, w_router, top_k: int, gate_up_q, gate_up_r, down_q, down_r,
+                                bits: int, out=None, sel_idx=None, sel_w=None, ws=None):
+    """x [T][H]; w_router [H][E]; row-scaled experts stacked: gate_up_q
+    [E][2F][H * bits / 8], gate_up_r [E][2F], down_q [E][H][F * bits / 8],
+    down_r [E][H]."""
+    t, hidden = x.shape
+    e = w_router.shape[1]
+    ffn = gate_up_q.shape[1] // 2
+    y = _out(out, (t, hidden), torch.float32, x)
+    si = _out(sel_idx, (t, top_k), torch.int32, x)
+    sw = _out(sel_w, (t, top_k), torch.float32, x)
+    need = qk_moe_workspace(t, hidden, e, top_k, ffn)
+    wsb = _ws(ws, need, x.device)
+    _check(load().qk_moe_route_and_apply_rowq(
+        bits, _dev(x, torch.float32, "x"), t, hidden, _dev(w_router, torch.float32, "w_router"), e,
+        top_k, _dev(gate_up_q, torch.uint8, "gate_up_q"), _dev(gate_up_r, torch.float32, "gate_up_r"),
+        _dev(down_q, torch.uint8, "down_q"), _dev(down_r, torch.float32, "down_r"), ffn,
+        _dev(y, torch.float32, "y"), _dev(si, torch.int32, "sel_idx"), _dev(sw, torch.float32, "sel_w"),
+        wsb.data_ptr(), need, _stream()), "qk_moe_route_and_apply_rowq")
     return y, si, sw

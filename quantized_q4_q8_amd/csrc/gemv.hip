@@ -65,6 +65,29 @@ __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+// Row-scaled int2 block (8 bytes in w.x, w.y): byte j holds elements j, j + 8,
+// j + 16, j + 24 in bits 0-1, 2-3, 4-5, 6-7, so shifting the two words by 0,
+// 2, 4, 6 and masking gives elements 0-7, 8-15, 16-23, 24-31 in order.
+__device__ __forceinline__ int dot_block2(const uint4 w, const uint4 x0, const uint4 x1, int s) {
+    const uint32_t m2 = 0x03030303u;
+    s = __builtin_amdgcn_sdot4((int)(w.x & m2), (int)x0.x, s, false);
+    s = __builtin_amdgcn_sdot4((int)(w.y & m2), (int)x0.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 2) & m2), (int)x0.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 2) & m2), (int)x0.w, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 4) & m2), (int)x1.x, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 4) & m2), (int)x1.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 6) & m2), (int)x1.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 6) & m2), (int)x1.w, s, false);
+    return s;
+}
+
 }  // namespace
 
 // Workgroup-wide RMSNorm / Q8_0 of one activation row into LDS.  Each lane
@@ -207,8 +230,11 @@ __host__ __device__ constexpr int rows_per_unit(int epi) {
 // every row.
 // KLOOP: K may exceed 64 * U blocks (the weights are then loaded step by
 // step); otherwise the whole row share is loaded at once.
-template <int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
-__global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
+// FMT: Q4_0 (fp16 scale per block), or row-scaled int4 / int2 (fp32 scale
+// per row): their block sums are dx * isum, and the row's scale multiplies
+// the row's total in the epilogue, once.
+template <int FMT, int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
+__device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double red[4];
     constexpr int RMAX = R;
@@ -231,10 +257,13 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     }
     if (nc <= 0) return;   // uniform over the workgroup
 
-    const int64_t k = a.k, nb = k / QBLK, kh = k / 2;
+    const int64_t k = a.k, nb = k / QBLK;
+    constexpr uint32_t BB = FMT == FMT_Q2_ROW ? 8u : 16u;   // weight bytes per 32-block
+    const uint32_t rowb = (uint32_t)nb * BB;
     const double* theta = a.rope_theta;   // read in place from the kernel arguments
     const uint8_t* __restrict__ wq = a.wq + (int64_t)g * a.wq_gstride;
     const uint16_t* __restrict__ wd = a.wd + (int64_t)g * a.wd_gstride;
+    const float* __restrict__ wr = FMT != FMT_Q4_0 ? a.wr + (int64_t)g * a.wr_gstride : nullptr;
 
     // physical row of register row j (j = unit * P + part)
     const int64_t ffn = a.ffn;
@@ -262,6 +291,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
 
         uint4 w[RMAX][U];
         float dw[RMAX][U];
+        float drs[RMAX];   // row scales (row-scaled formats)
         // 32-bit offsets from the (uniform) matrix base: one matrix is below 4 GiB
         auto load_w = [&](int64_t b0) {
 #pragma unroll
@@ -270,16 +300,26 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint32_t b = (uint32_t)b0 + u * WAVE + lane;
+                    dw[j][u] = 0.0f;
                     if (rvalid(j) && b < (uint32_t)nb) {
-                        w[j][u] = load_stream16(wq + (row * (uint32_t)kh + b * 16u));
-                        dw[j][u] = h2f(*reinterpret_cast<const uint16_t*>(
-                            reinterpret_cast<const char*>(wd) + (row * (uint32_t)nb + b) * 2u));
+                        if (FMT == FMT_Q2_ROW) {
+                            const uint2 v = load_stream8(wq + (row * rowb + b * BB));
+                            w[j][u] = make_uint4(v.x, v.y, 0u, 0u);
+                        } else {
+                            w[j][u] = load_stream16(wq + (row * rowb + b * BB));
+                        }
+                        if (FMT == FMT_Q4_0)
+                            dw[j][u] = h2f(*reinterpret_cast<const uint16_t*>(
+                                reinterpret_cast<const char*>(wd) + (row * (uint32_t)nb + b) * 2u));
                     } else {
                         w[j][u] = make_uint4(0, 0, 0, 0);
-                        dw[j][u] = 0.0f;
                     }
                 }
             }
+        };
+        auto load_rs = [&]() {
+#pragma unroll
+            for (int j = 0; j < RMAX; ++j) drs[j] = (FMT != FMT_Q4_0 && rvalid(j)) ? wr[prow(j)] : 0.0f;
         };
 
         if (cc > 0) lds_barrier();   // the previous pass finished reading LDS
@@ -320,6 +360,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
             xds = 0.0f;
             if (threadIdx.x < totd) xds = h2f(a.xd[col_row((int)(threadIdx.x / nb)) * nb + threadIdx.x % nb]);
             load_w(0);
+            if (FMT != FMT_Q4_0) load_rs();
 #pragma unroll
             for (int p = 0; p < XREG; ++p) {
                 const int64_t i = threadIdx.x + (int64_t)p * 256;
@@ -352,13 +393,19 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
                     const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
                     const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 16);
                     const float dx = lxd[(size_t)m * nb + b];
-                    const int s0 = -8 * byte_sum(x0, x1);
+                    const int s0 = (FMT == FMT_Q2_ROW ? -2 : -8) * byte_sum(x0, x1);
 #pragma unroll
                     for (int j = 0; j < RMAX; ++j) {
-                        // dw * dx is exact in fp32 (two fp16 values); times the
-                        // int32 block dot it is exact in fp64
-                        const int sdot = dot_block(w[j][u], x0, x1, s0);
-                        acc[j][m] = fma((double)(dw[j][u] * dx), (double)sdot, acc[j][m]);
+                        if (FMT == FMT_Q4_0) {
+                            // dw * dx is exact in fp32 (two fp16 values); times
+                            // the int32 block dot it is exact in fp64
+                            const int sdot = dot_block(w[j][u], x0, x1, s0);
+                            acc[j][m] = fma((double)(dw[j][u] * dx), (double)sdot, acc[j][m]);
+                        } else {
+                            const int sdot = FMT == FMT_Q2_ROW ? dot_block2(w[j][u], x0, x1, s0)
+                                                               : dot_block(w[j][u], x0, x1, s0);
+                            acc[j][m] = fma((double)dx, (double)sdot, acc[j][m]);
+                        }
                     }
                 }
             }
@@ -393,6 +440,16 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
         }
         const int r = base + kk;
         const int m = r / RMAX, j = r % RMAX;
+        if (FMT != FMT_Q4_0) {   // the row scales, applied once to the row totals
+            float d1 = drs[0], d2 = drs[0];
+#pragma unroll
+            for (int q = 1; q < RMAX; ++q) {
+                if (j == q) d1 = drs[q];
+                if ((j ^ 1) == q) d2 = drs[q];
+            }
+            s *= (double)d1;
+            if (P == 2) s2 *= (double)d2;
+        }
         constexpr int OWN = N >= 4 ? 16 : (N == 2 ? 32 : 64);   // lanes sharing one row's sums
         const bool owner = (NV > 1 ? kk < NV : (lane & (OWN - 1)) == 0) && rvalid(j) && cc + m < nc;
         const int64_t row = prow(j);
@@ -467,6 +524,17 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
             }
         }
     }
+}
+
+template <int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
+__global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
+    gemv_body<FMT_Q4_0, M, R, U, EPI, PRO, KC, KLOOP>(a);
+}
+
+// Row-scaled int4 / int2 weights: no prologue, store or SwiGLU epilogue.
+template <int FMT, int M, int R, int U, int EPI, bool KLOOP>
+__global__ __launch_bounds__(256) void k_gemv_rowq(const GemvArgs a) {
+    gemv_body<FMT, M, R, U, EPI, PRO_NONE, 1, KLOOP>(a);
 }
 
 // idx[c] = row of the largest partial of column c (ties to the lowest row).
@@ -548,61 +616,68 @@ int pick_cols(const GemvArgs& a, int epi) {
     return M;
 }
 
-template <int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
+template <int FMT, int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
 void launch_cfg(const GemvArgs& a, hipStream_t s) {
     const int64_t units = units_of(a, EPI);
     const int64_t per_wg = 4 * (int64_t)(R / rows_per_unit(EPI));
     dim3 grid((unsigned)((units + per_wg - 1) / per_wg), (unsigned)a.groups);
-    hipLaunchKernelGGL((k_gemv<M, R, U, EPI, PRO, KC, KLOOP>), grid, dim3(256),
-                       lds_bytes(EPI, M, a.k, R), s, a);
+    if constexpr (FMT == FMT_Q4_0) {
+        hipLaunchKernelGGL((k_gemv<M, R, U, EPI, PRO, KC, KLOOP>), grid, dim3(256),
+                           lds_bytes(EPI, M, a.k, R), s, a);
+    } else {
+        static_assert(PRO == PRO_NONE && (EPI == EPI_STORE || EPI == EPI_SWIGLU),
+                      "row-scaled weights: no prologue, store or SwiGLU epilogue");
+        hipLaunchKernelGGL((k_gemv_rowq<FMT, M, R, U, EPI, KLOOP>), grid, dim3(256),
+                           lds_bytes(EPI, M, a.k, R), s, a);
+    }
 }
 
-template <int M, int U, int EPI, int PRO, int KC, bool KLOOP>
+template <int FMT, int M, int U, int EPI, int PRO, int KC, bool KLOOP>
 void launch_r(const GemvArgs& a, hipStream_t s) {
     constexpr int P = rows_per_unit(EPI);
     const int R = pick_rows(EPI, PRO, M, a.k, units_of(a, EPI) * a.groups);
     if constexpr (M <= 2) {
-        if (R >= 4) { launch_cfg<M, 4, U, EPI, PRO, KC, KLOOP>(a, s); return; }
+        if (R >= 4) { launch_cfg<FMT, M, 4, U, EPI, PRO, KC, KLOOP>(a, s); return; }
     }
     if constexpr (P == 1) {
-        if (R == 1) { launch_cfg<M, 1, U, EPI, PRO, KC, KLOOP>(a, s); return; }
+        if (R == 1) { launch_cfg<FMT, M, 1, U, EPI, PRO, KC, KLOOP>(a, s); return; }
     }
-    launch_cfg<M, 2, U, EPI, PRO, KC, KLOOP>(a, s);
+    launch_cfg<FMT, M, 2, U, EPI, PRO, KC, KLOOP>(a, s);
 }
 
 // Prologue chunks (2048 values each) held in registers: one for K <= 2048.
-template <int M, int U, int EPI, int PRO, bool KLOOP>
+template <int FMT, int M, int U, int EPI, int PRO, bool KLOOP>
 void launch_kc(const GemvArgs& a, hipStream_t s) {
     if constexpr (PRO == PRO_NONE) {
-        launch_r<M, U, EPI, PRO, 1, KLOOP>(a, s);
+        launch_r<FMT, M, U, EPI, PRO, 1, KLOOP>(a, s);
     } else {
-        if (a.k <= 2048) launch_r<M, U, EPI, PRO, 1, KLOOP>(a, s);
-        else launch_r<M, U, EPI, PRO, PRO_CHUNKS, KLOOP>(a, s);
+        if (a.k <= 2048) launch_r<FMT, M, U, EPI, PRO, 1, KLOOP>(a, s);
+        else launch_r<FMT, M, U, EPI, PRO, PRO_CHUNKS, KLOOP>(a, s);
     }
 }
 
 // Blocks per lane per step: one for K <= 2048, three up to K = 6144 (one
 // step either way); longer rows (no prologue) loop over steps of three.
-template <int M, int EPI, int PRO>
+template <int FMT, int M, int EPI, int PRO>
 void launch_u(const GemvArgs& a, hipStream_t s) {
     const int64_t nb = a.k / QBLK;
     if (nb <= WAVE) {
-        launch_kc<M, 1, EPI, PRO, false>(a, s);
+        launch_kc<FMT, M, 1, EPI, PRO, false>(a, s);
     } else if (nb <= 3 * WAVE) {
-        launch_kc<M, 3, EPI, PRO, false>(a, s);
+        launch_kc<FMT, M, 3, EPI, PRO, false>(a, s);
     } else {
         if constexpr (PRO == PRO_NONE && (EPI == EPI_STORE || EPI == EPI_SWIGLU))
-            launch_kc<M, 3, EPI, PRO, true>(a, s);
+            launch_kc<FMT, M, 3, EPI, PRO, true>(a, s);
     }
 }
 
-template <int EPI, int PRO>
+template <int EPI, int PRO, int FMT = FMT_Q4_0>
 void launch_m(const GemvArgs& a, hipStream_t s) {
     switch (pick_cols(a, EPI)) {
-        case 1: launch_u<1, EPI, PRO>(a, s); break;
-        case 2: launch_u<2, EPI, PRO>(a, s); break;
-        case 4: launch_u<4, EPI, PRO>(a, s); break;
-        default: launch_u<8, EPI, PRO>(a, s); break;
+        case 1: launch_u<FMT, 1, EPI, PRO>(a, s); break;
+        case 2: launch_u<FMT, 2, EPI, PRO>(a, s); break;
+        case 4: launch_u<FMT, 4, EPI, PRO>(a, s); break;
+        default: launch_u<FMT, 8, EPI, PRO>(a, s); break;
     }
 }
 
@@ -632,6 +707,19 @@ int launch_gemv(const GemvArgs& a, int epi, hipStream_t s, int pro) {
         return QK_ESHAPE;
     if (pro != PRO_NONE && !gemv_prologue_fits(a.k, a.max_cols)) return QK_ESHAPE;
     if (epi == EPI_QKV && (a.hd % 2 || a.q_rows % 2 || a.kv_rows % 2)) return QK_ESHAPE;
+    if (a.fmt != FMT_Q4_0) {
+        if (pro != PRO_NONE || (epi != EPI_STORE && epi != EPI_SWIGLU)) return QK_ESHAPE;
+        if (a.fmt == FMT_Q4_ROW) {
+            if (epi == EPI_SWIGLU) launch_m<EPI_SWIGLU, PRO_NONE, FMT_Q4_ROW>(a, s);
+            else launch_m<EPI_STORE, PRO_NONE, FMT_Q4_ROW>(a, s);
+        } else if (a.fmt == FMT_Q2_ROW) {
+            if (epi == EPI_SWIGLU) launch_m<EPI_SWIGLU, PRO_NONE, FMT_Q2_ROW>(a, s);
+            else launch_m<EPI_STORE, PRO_NONE, FMT_Q2_ROW>(a, s);
+        } else {
+            return QK_EINVAL;
+        }
+        return qk_launch_status();
+    }
     if (epi == EPI_SWIGLU) {
         if (pro == PRO_RMSNORM) launch_m<EPI_SWIGLU, PRO_RMSNORM>(a, s);
         else launch_m<EPI_SWIGLU, PRO_NONE>(a, s);

@@ -24,11 +24,18 @@ enum GemvPrologue : int {
 // col_off is null).  Column c reads activation row col_idx[c] (c when col_idx
 // is null) and writes output row c: y[c * ldy + row].  With a residual,
 // y[c * ldy + row] = residual[c * ldr + row] + acc (y may equal residual).
+// Weight formats of the GEMV: Q4_0 (fp16 scale per 32-block), row-scaled
+// int4 and int2 (fp32 scale per row; int4 in the Q4_0 nibble order, int2 with
+// elements j, j + 8, j + 16, j + 24 of a 32-block in byte j).
+enum { FMT_Q4_0 = 0, FMT_Q4_ROW = 1, FMT_Q2_ROW = 2 };
+
 struct GemvArgs {
     const uint8_t* wq;
-    const uint16_t* wd;
+    const uint16_t* wd;      // FMT_Q4_0 block scales
+    const float* wr;         // row-scaled formats: scales [n] per group
+    int32_t fmt;
     int64_t n, k;          // rows (physical) and K of one group's matrix
-    int64_t wq_gstride, wd_gstride;
+    int64_t wq_gstride, wd_gstride, wr_gstride;
     const int8_t* xq;
     const uint16_t* xd;
     const int32_t* col_off;  // [groups + 1] or null

@@ -226,12 +226,20 @@ extern "C" size_t qk_moe_workspace(int64_t tokens, int64_t hidden, int64_t n_exp
     return moe_layout(nullptr, tokens, hidden, n_experts, top_k, ffn).total;
 }
 
-extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden,
-                                   const float* w_router, int64_t n_experts, int32_t top_k,
-                                   const uint8_t* gate_up_q, const uint16_t* gate_up_d,
-                                   const uint8_t* down_q, const uint16_t* down_d, int64_t ffn,
-                                   float* y, int32_t* sel_idx, float* sel_w, void* ws,
-                                   size_t ws_bytes, void* stream) {
+namespace {
+
+// Expert weights of one format, stacked over the experts.
+struct ExpertWeights {
+    int fmt;                   // FMT_Q4_0, FMT_Q4_ROW or FMT_Q2_ROW
+    const uint8_t* gu_q;       // [E][2F] rows of H weights
+    const void* gu_s;          // Q4_0: fp16 [E][2F][H/32]; row-scaled: fp32 [E][2F]
+    const uint8_t* dn_q;       // [E][H] rows of F weights
+    const void* dn_s;          // Q4_0: fp16 [E][H][F/32]; row-scaled: fp32 [E][H]
+};
+
+int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_router,
+              int64_t n_experts, int32_t top_k, const ExpertWeights& ew, int64_t ffn, float* y,
+              int32_t* sel_idx, float* sel_w, void* ws, size_t ws_bytes, hipStream_t s) {
     QK_REQUIRE(tokens >= 0 && hidden > 0 && ffn > 0, QK_EINVAL);
     QK_REQUIRE(n_experts > 0 && n_experts <= 1024 && top_k > 0 && top_k <= 32 &&
                    top_k <= n_experts,
@@ -239,16 +247,17 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     QK_REQUIRE(hidden % QBLK == 0 && ffn % QBLK == 0, QK_ESHAPE);
     QK_REQUIRE(tokens * top_k <= INT32_MAX, QK_EINVAL);
     if (tokens == 0) return QK_OK;
-    QK_REQUIRE(x && w_router && gate_up_q && gate_up_d && down_q && down_d && y && sel_idx && sel_w,
+    QK_REQUIRE(x && w_router && ew.gu_q && ew.gu_s && ew.dn_q && ew.dn_s && y && sel_idx && sel_w,
                QK_EINVAL);
-    QK_REQUIRE(QK_ALIGNED(x, 16) && QK_ALIGNED(y, 16) && QK_ALIGNED(gate_up_q, 16) &&
-                   QK_ALIGNED(down_q, 16),
+    QK_REQUIRE(QK_ALIGNED(x, 16) && QK_ALIGNED(y, 16) && QK_ALIGNED(ew.gu_q, 16) &&
+                   QK_ALIGNED(ew.dn_q, 16) && QK_ALIGNED(ew.gu_s, ew.fmt == FMT_Q4_0 ? 2 : 4) &&
+                   QK_ALIGNED(ew.dn_s, ew.fmt == FMT_Q4_0 ? 2 : 4),
                QK_EALIGN);
     const MoeWs w = moe_layout(ws, tokens, hidden, n_experts, top_k, ffn);
     QK_REQUIRE(ws && ws_bytes >= w.total, QK_EWORKSPACE);
-    hipStream_t s = (hipStream_t)stream;
     const int64_t T = tokens, H = hidden, E = n_experts, F = ffn, P = T * top_k;
     const int64_t slices = (H + RSLICE - 1) / RSLICE;
+    const int64_t bpb = ew.fmt == FMT_Q2_ROW ? 8 : 16;   // weight bytes per 32-block
 
     hipLaunchKernelGGL(k_router, dim3((unsigned)((E + 255) / 256), (unsigned)((T + RT - 1) / RT),
                                       (unsigned)slices),
@@ -261,8 +270,13 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     if (rc) return rc;
 
     GemvArgs g{};
-    g.wq = gate_up_q; g.wd = gate_up_d; g.n = 2 * F; g.k = H;
-    g.wq_gstride = 2 * F * (H / 2); g.wd_gstride = 2 * F * (H / QBLK);
+    g.fmt = ew.fmt; g.wq = ew.gu_q; g.n = 2 * F; g.k = H;
+    g.wq_gstride = 2 * F * (H / QBLK) * bpb;
+    if (ew.fmt == FMT_Q4_0) {
+        g.wd = static_cast<const uint16_t*>(ew.gu_s); g.wd_gstride = 2 * F * (H / QBLK);
+    } else {
+        g.wr = static_cast<const float*>(ew.gu_s); g.wr_gstride = 2 * F;
+    }
     g.xq = w.xq; g.xd = w.xd; g.col_off = w.off; g.col_idx = w.col_tok;
     g.m = 0; g.groups = (int32_t)E; g.y = w.h; g.ldy = F; g.residual = nullptr; g.ldr = 0;
     g.ffn = F; g.max_cols = (int32_t)std::min<int64_t>(8, (P + E - 1) / E);
@@ -272,8 +286,13 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     if (rc) return rc;
 
     GemvArgs d{};
-    d.wq = down_q; d.wd = down_d; d.n = H; d.k = F;
-    d.wq_gstride = H * (F / 2); d.wd_gstride = H * (F / QBLK);
+    d.fmt = ew.fmt; d.wq = ew.dn_q; d.n = H; d.k = F;
+    d.wq_gstride = H * (F / QBLK) * bpb;
+    if (ew.fmt == FMT_Q4_0) {
+        d.wd = static_cast<const uint16_t*>(ew.dn_s); d.wd_gstride = H * (F / QBLK);
+    } else {
+        d.wr = static_cast<const float*>(ew.dn_s); d.wr_gstride = H;
+    }
     d.xq = w.hq; d.xd = w.hd; d.col_off = w.off; d.col_idx = nullptr;
     d.m = 0; d.groups = (int32_t)E; d.y = w.ys; d.ldy = H; d.residual = nullptr; d.ldr = 0;
     d.ffn = 0; d.max_cols = g.max_cols;
@@ -283,4 +302,30 @@ extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidde
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, s,
                        w.ys, H, top_k, w.slot, sel_w, y);
     return qk_launch_status();
+}
+
+}  // namespace
+
+extern "C" int moe_route_and_apply(const float* x, int64_t tokens, int64_t hidden,
+                                   const float* w_router, int64_t n_experts, int32_t top_k,
+                                   const uint8_t* gate_up_q, const uint16_t* gate_up_d,
+                                   const uint8_t* down_q, const uint16_t* down_d, int64_t ffn,
+                                   float* y, int32_t* sel_idx, float* sel_w, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    const ExpertWeights ew{FMT_Q4_0, gate_up_q, gate_up_d, down_q, down_d};
+    return moe_apply(x, tokens, hidden, w_router, n_experts, top_k, ew, ffn, y, sel_idx, sel_w, ws,
+                     ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" int qk_moe_route_and_apply_rowq(int32_t bits, const float* x, int64_t tokens,
+                                           int64_t hidden, const float* w_router,
+                                           int64_t n_experts, int32_t top_k,
+                                           const uint8_t* gate_up_q, const float* gate_up_r,
+                                           const uint8_t* down_q, const float* down_r,
+                                           int64_t ffn, float* y, int32_t* sel_idx, float* sel_w,
+                                           void* ws, size_t ws_bytes, void* stream) {
+    QK_REQUIRE(bits == 4 || bits == 2, QK_EINVAL);
+    const ExpertWeights ew{bits == 4 ? FMT_Q4_ROW : FMT_Q2_ROW, gate_up_q, gate_up_r, down_q, down_r};
+    return moe_apply(x, tokens, hidden, w_router, n_experts, top_k, ew, ffn, y, sel_idx, sel_w, ws,
+                     ws_bytes, (hipStream_t)stream);
 }

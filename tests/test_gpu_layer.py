@@ -203,6 +203,31 @@ def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     assert np.allclose(w_g.sum(1), 1.0, atol=1e-6)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (16, 6144, 16, 2048, 8)])
+def test_moe_rowq_matches_oracle(gpu_lib, bits, T, H, E, F, k):
+    """The MoE layer with row-scaled int4 / int2 experts (the last case has
+    the expert shape of the MoE workload, 16 experts)."""
+    qk = gpu_lib
+    say(f"qk_moe_route_and_apply_rowq bits={bits} T={T} H={H} E={E} F={F} k={k}")
+    seed = 60 + T
+    x = synth.normal(seed, W.TID_X, (T, H))
+    wr = synth.normal(seed, W.TID_ROUTER, (H, E), 0.02)
+    gu, dn = experts_f32(seed, E, H, F)
+    guq, gur = map(np.stack, zip(*[oracle.quantize_rowq(a, bits) for a in gu]))
+    dnq, dnr = map(np.stack, zip(*[oracle.quantize_rowq(a, bits) for a in dn]))
+    out, sel, w = oracle.moe_route_and_apply_rowq(x, wr, k, guq, gur, dnq, dnr, bits)
+    _, _, logits = oracle.moe_route(x, wr, k, return_logits=True)
+    y, sg, wg = qk.qk_moe_route_and_apply_rowq(dev(x), dev(wr), k, dev(guq), dev(gur), dev(dnq),
+                                               dev(dnr), bits)
+    sel_g, w_g = host(sg), host(wg)
+    check_routing(sel_g, w_g, sel, w, logits)
+    if np.array_equal(sel_g, sel):
+        assert rel_err(host(y), out) < LAYER_TOL
+        assert_same_fp32(host(y), out)
+    assert all(len(set(r)) == k for r in sel_g)
+
+
 def test_moe_zero_router_ties(gpu_lib):
     qk = gpu_lib
     T, H, E, F, k = 4, 64, 12, 32, 5

@@ -98,6 +98,54 @@ def test_qmatmul_matches_oracle(gpu_lib, n, k, m):
     assert_same_fp32(host(y), ref)
 
 
+# ------------------------------------------------- row-scaled int4 / int2
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("n,k", [(7, 64), (384, 256), (2048, 6144), (33, 2048)])
+def test_quantize_rowq_bit_exact(gpu_lib, bits, n, k):
+    qk = gpu_lib
+    say(f"qk_quantize_rowq bits={bits} n={n} k={k}")
+    w = synth.normal(140, bits * 100 + n, (n, k), 0.02)
+    w[min(3, n - 1)] = 0.0                                   # a zero row
+    q, r = qk.qk_quantize_rowq(dev(w), bits)
+    oq, orr = oracle.quantize_rowq(w, bits)
+    assert np.array_equal(host(q, np.uint8), oq)
+    assert np.array_equal(host(r), orr)
+
+
+ROWQ_MM = [(5, 32, 1), (64, 2048, 3), (37, 704, 2), (2048, 6144, 1), (300, 8192, 4), (96, 256, 13),
+           (4096, 2048, 8)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("n,k,m", ROWQ_MM)
+def test_qmatmul_rowq_matches_oracle(gpu_lib, bits, n, k, m):
+    """Row-scaled weights through the GEMV: single and several columns,
+    ragged rows, rows past one load step (k 8192), and more than 8 columns
+    (two passes)."""
+    qk = gpu_lib
+    say(f"qk_qmatmul_rowq_q8_0 bits={bits} n={n} k={k} m={m}")
+    w = synth.normal(141, bits * 100 + n + 3 * k, (n, k), 0.02)
+    x = synth.normal(142, n + 5 * k + m, (m, k))
+    wq, wr = oracle.quantize_rowq(w, bits)
+    xq, xd = oracle.quantize_q8_0(x)
+    y = qk.qk_qmatmul_rowq_q8_0(dev(wq), dev(wr), dev(xq), dev(xd), bits)
+    ref = oracle.qmatmul_rowq(wq, wr, xq, xd, bits)
+    assert rel_err(host(y), ref) < 1e-5
+    assert_same_fp32(host(y), ref)
+
+
+def test_rowq_rejects_bad_bits(gpu_lib):
+    qk = gpu_lib
+    L = qk.load()
+    w = torch.zeros((2, 64), dtype=torch.float32, device="cuda")
+    q = torch.zeros((2, 32), dtype=torch.uint8, device="cuda")
+    r = torch.zeros(2, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for bits in (0, 3, 8):
+        assert L.qk_quantize_rowq(bits, w.data_ptr(), 2, 64, q.data_ptr(), r.data_ptr(), s) == qk.QK_EINVAL
+    assert L.qk_quantize_rowq(4, w.data_ptr(), 2, 48, q.data_ptr(), r.data_ptr(), s) == qk.QK_ESHAPE
+
+
 def test_qmatmul_workload_seeded(gpu_lib):
     """The standalone matmul workload as generated (seed 1): W 5632x2048 and
     the transposed-shape 2048x5632, at batch 1 and 8, quantized on the GPU."""
