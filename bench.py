@@ -43,6 +43,9 @@ def parse():
                     help="decode (the headline line); the others measure decode past an "
                          "8192-row ring cache and the standalone matmul, prefill, MoE and "
                          "sampler workloads")
+    ap.add_argument("--codec", default="q4_0", choices=["q4_0", "int4row", "int2row"],
+                    help="weight format of the matmul and moe workloads: Q4_0 (fp16 scale per "
+                         "32-block) or row-scaled int4 / int2 (fp32 scale per row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
@@ -358,21 +361,30 @@ def run_matmul(args):
     spec = W.MATMUL
     rows = []
     dev = torch.device("cuda")
+    bits = {"q4_0": 0, "int4row": 4, "int2row": 2}[args.codec]
     for idx, (n, k) in enumerate(spec["shapes"]):
-        wq, wd = qk.qk_quantize_q4_0(to_device(W.matmul_weight_f32(spec["seed"], idx, n, k)))
-        wbytes = n * k * 9 // 16
+        wf = to_device(W.matmul_weight_f32(spec["seed"], idx, n, k))
+        if bits:   # row-scaled: codes [n][k bits / 8] and fp32 scales [n]
+            wq, wd = qk.qk_quantize_rowq(wf, bits)
+            wbytes = n * k * bits // 8 + n * 4
+            mm = lambda a, b, xq, xd, out: qk.qk_qmatmul_rowq_q8_0(a, b, xq, xd, bits, out=out)  # noqa: E731
+        else:
+            wq, wd = qk.qk_quantize_q4_0(wf)
+            wbytes = n * k * 9 // 16
+            mm = qk.qmatmul_q4_0_q8_0
+        del wf
         # distinct copies filling 1 GiB, so that a launch cannot hit the 256 MB
         # memory-side cache left warm by the previous one
         copies = -(-(1 << 30) // wbytes)
-        wq_all = wq.unsqueeze(0).repeat(copies, 1, 1)
-        wd_all = wd.unsqueeze(0).repeat(copies, 1, 1)
+        wq_all = wq.unsqueeze(0).repeat(copies, *([1] * wq.dim()))
+        wd_all = wd.unsqueeze(0).repeat(copies, *([1] * wd.dim()))
         for m in spec["batches"]:
             xq, xd = qk.quantize_q8_0(to_device(W.matmul_input_f32(spec["seed"], idx, m, k)))
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             nbytes = wbytes + m * k * 34 // 32 + m * n * 4
-            cold = graph_time_us(lambda: [qk.qmatmul_q4_0_q8_0(wq_all[c], wd_all[c], xq, xd, out=y)
+            cold = graph_time_us(lambda: [mm(wq_all[c], wd_all[c], xq, xd, out=y)
                                           for c in range(copies)], copies, max(2, args.steps))
-            hot = graph_time_us(lambda: [qk.qmatmul_q4_0_q8_0(wq, wd, xq, xd, out=y)
+            hot = graph_time_us(lambda: [mm(wq, wd, xq, xd, out=y)
                                          for _ in range(copies)], copies, max(2, args.steps))
             rec = {"n": n, "k": k, "m": m, "bytes_per_launch": nbytes,
                    "cold_us": round(cold, 3), "cold_GBps": round(nbytes / cold / 1e3, 1),
@@ -384,13 +396,15 @@ def run_matmul(args):
         del wq_all, wd_all
         torch.cuda.empty_cache()
     head = rows[0]
-    out = base_line(args, "Q4_0 x Q8_0 GEMV GB/s, W 5632x2048 x x[2048], cold memory-side cache",
+    wname = {"q4_0": "Q4_0", "int4row": "row-scaled int4", "int2row": "row-scaled int2"}[args.codec]
+    out = base_line(args, f"{wname} x Q8_0 GEMV GB/s, W 5632x2048 x x[2048], cold memory-side cache",
                     head["cold_GBps"], "GB/s", head["cold_us"] / 1e3,
-                    "q4_0 x q8_0 (int32 block dots, fp64 accumulate)",
+                    f"{args.codec} x q8_0 (int32 block dots, fp64 accumulate)",
                     {"workload": "standalone matmul: W 5632x2048 and 2048x5632, batch 1 and 8",
+                     "codec": args.codec,
                      "copies": "1 GiB of distinct weight copies rotated per launch",
                      "parallelism": "single GPU"})
-    out["roofline"] = {"bound": "hbm", "kernel": "k_gemv (M=1, store epilogue)",
+    out["roofline"] = {"bound": "hbm", "kernel": "k_gemv_rowq (M=1, store epilogue)" if bits else "k_gemv (M=1, store epilogue)",
                        "achieved": head["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(head["cold_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
                        "bytes_per_launch": head["bytes_per_launch"], "avg_us": head["cold_us"]}
@@ -398,11 +412,16 @@ def run_matmul(args):
     if not args.no_cpu_baseline:
         import oracle
         w = W.matmul_weight_f32(spec["seed"], 0, 5632, 2048)
-        owq, owd = oracle.quantize_q4_0(w)
         xq, xd = oracle.quantize_q8_0(W.matmul_input_f32(spec["seed"], 0, 1, 2048))
+        if bits:
+            owq, owr = oracle.quantize_rowq(w, bits)
+            omm = lambda: oracle.qmatmul_rowq(owq, owr, xq, xd, bits)  # noqa: E731
+        else:
+            owq, owd = oracle.quantize_q4_0(w)
+            omm = lambda: oracle.qmatmul(owq, owd, xq, xd)  # noqa: E731
         t0, n = time.perf_counter(), 0
         while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0) or n == 0:
-            oracle.qmatmul(owq, owd, xq, xd)
+            omm()
             n += 1
         dt = (time.perf_counter() - t0) / n
         threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -508,15 +527,26 @@ def run_moe(args):
     spec = W.MOE
     seed, T, H, E, F, k = spec["seed"], spec["tokens"], spec["hidden"], spec["experts"], spec["ffn"], spec["top_k"]
     dev = torch.device("cuda")
+    bits = {"q4_0": 0, "int4row": 4, "int2row": 2}[args.codec]
     t0 = time.time()
-    guq = torch.empty((E, 2 * F, H // 2), dtype=torch.uint8, device=dev)
-    gud = torch.empty((E, 2 * F, H // 32), dtype=torch.int16, device=dev)
-    dnq = torch.empty((E, H, F // 2), dtype=torch.uint8, device=dev)
-    dnd = torch.empty((E, H, F // 32), dtype=torch.int16, device=dev)
+    if bits:   # row-scaled experts: codes and one fp32 scale per row
+        guq = torch.empty((E, 2 * F, H * bits // 8), dtype=torch.uint8, device=dev)
+        gud = torch.empty((E, 2 * F), dtype=torch.float32, device=dev)
+        dnq = torch.empty((E, H, F * bits // 8), dtype=torch.uint8, device=dev)
+        dnd = torch.empty((E, H), dtype=torch.float32, device=dev)
+        quant = lambda w, q, d: qk.qk_quantize_rowq(w, bits, out_q=q, out_r=d)  # noqa: E731
+        per_expert = 2 * F * (H * bits // 8 + 4) + H * (F * bits // 8 + 4)
+    else:
+        guq = torch.empty((E, 2 * F, H // 2), dtype=torch.uint8, device=dev)
+        gud = torch.empty((E, 2 * F, H // 32), dtype=torch.int16, device=dev)
+        dnq = torch.empty((E, H, F // 2), dtype=torch.uint8, device=dev)
+        dnd = torch.empty((E, H, F // 32), dtype=torch.int16, device=dev)
+        quant = lambda w, q, d: qk.qk_quantize_q4_0(w, out_q=q, out_d=d)  # noqa: E731
+        per_expert = 3 * F * H * 9 // 16
     for e in range(E):
         gu, dn = W.expert_weights_f32(seed, e, H, F)
-        qk.qk_quantize_q4_0(to_device(gu), out_q=guq[e], out_d=gud[e])
-        qk.qk_quantize_q4_0(to_device(dn), out_q=dnq[e], out_d=dnd[e])
+        quant(to_device(gu), guq[e], gud[e])
+        quant(to_device(dn), dnq[e], dnd[e])
     torch.cuda.synchronize()
     log(f"{E} experts resident after {time.time() - t0:.1f}s")
     x = to_device(normal(seed, W.TID_X, (T, H)))
@@ -525,18 +555,25 @@ def run_moe(args):
     sel = torch.empty((T, k), dtype=torch.int32, device=dev)
     sw = torch.empty((T, k), dtype=torch.float32, device=dev)
     ws = torch.empty(qk.qk_moe_workspace(T, H, E, k, F), dtype=torch.uint8, device=dev)
-    call = lambda: qk.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd, out=y, sel_idx=sel, sel_w=sw, ws=ws)
+    if bits:
+        call = lambda: qk.qk_moe_route_and_apply_rowq(x, wr, k, guq, gud, dnq, dnd, bits, out=y,  # noqa: E731
+                                                      sel_idx=sel, sel_w=sw, ws=ws)
+    else:
+        call = lambda: qk.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd, out=y, sel_idx=sel,  # noqa: E731
+                                              sel_w=sw, ws=ws)
     call()
     torch.cuda.synchronize()
     distinct = int(torch.unique(sel).numel())
     us = graph_time_us(call, 1, max(3, args.steps))
-    per_expert = 3 * F * H * 9 // 16
     nbytes = distinct * per_expert + H * E * 4 + 2 * T * H * 4
     gbs = nbytes / us / 1e3
-    log(f"moe: {us:.1f} us per layer, {distinct} distinct experts, {gbs:.0f} GB/s")
-    out = base_line(args, "MoE layer GB/s (256 resident Q4_0 experts, 64 tokens, top-8)", gbs, "GB/s",
-                    us / 1e3, "q4_0 x q8_0 (int32 block dots, fp64 accumulate); fp64 router",
+    log(f"moe ({args.codec}): {us:.1f} us per layer, {distinct} distinct experts of {per_expert} B, "
+        f"{gbs:.0f} GB/s")
+    wname = {"q4_0": "Q4_0", "int4row": "row-scaled int4", "int2row": "row-scaled int2"}[args.codec]
+    out = base_line(args, f"MoE layer GB/s (256 resident {wname} experts, 64 tokens, top-8)", gbs, "GB/s",
+                    us / 1e3, f"{args.codec} x q8_0 (int32 block dots, fp64 accumulate); fp64 router",
                     {"workload": "moe layer: hidden 6144, 256 experts x SwiGLU 2048, 64 tokens, top-8",
+                     "codec": args.codec, "bytes_per_expert": per_expert,
                      "distinct_experts": distinct, "parallelism": "single GPU"})
     out["us_per_layer"] = round(us, 2)
     out["roofline"] = {"bound": "hbm", "kernel": "whole MoE layer (router, top-k, grouping, grouped GEMVs, combine)",
@@ -551,12 +588,24 @@ def run_moe(args):
         sel_o, w_o = oracle.moe_route(xs, wrh, k)
         for r in range(k):
             gu, dn = W.expert_weights_f32(seed, int(sel_o[0, r]), H, F)
-            experts.append(oracle.quantize_q4_0(gu) + oracle.quantize_q4_0(dn))
+            if bits:
+                experts.append(oracle.quantize_rowq(gu, bits) + oracle.quantize_rowq(dn, bits))
+            else:
+                experts.append(oracle.quantize_q4_0(gu) + oracle.quantize_q4_0(dn))
+
+        def expert_ffn(x1, gq, gs, dq, ds):
+            if not bits:
+                return oracle.moe_expert_ffn(x1, gq, gs, dq, ds)
+            xq, xd = oracle.quantize_q8_0(x1[None])
+            gu = oracle.qmatmul_rowq(gq, gs, xq, xd, bits)[0]
+            hq, hd = oracle.quantize_q8_0(oracle.swiglu(gu[:F], gu[F:])[None])
+            return oracle.qmatmul_rowq(dq, ds, hq, hd, bits)[0]
+
         t1 = time.perf_counter()
         sel_o, w_o = oracle.moe_route(xs, wrh, k)
         acc = np.zeros(H)
         for r in range(k):
-            acc += w_o[0, r] * oracle.moe_expert_ffn(xs[0], *experts[r])
+            acc += w_o[0, r] * expert_ffn(xs[0], *experts[r])
         dt = time.perf_counter() - t1
         threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         out["cpu_baseline"] = {"value": round(8 * per_expert / dt / 1e9, 3), "unit": "GB/s", "cores": threads,

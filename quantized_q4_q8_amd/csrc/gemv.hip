@@ -585,12 +585,14 @@ size_t stage_bytes(int M, int64_t k) {
 // Physical rows per wave.  Kernels that stage their activations with a
 // fused RMSNorm prologue run two units per wave (fewer workgroups repeat the
 // prologue); the others one unit per wave until the launch has more than
-// 8192 units, then two, then four (two at most for 4 or 8 columns per pass
-// or rows longer than 64 blocks).
+// 8192 units, then two, then four (two at most for 4 or 8 columns per pass,
+// or for Q4_0 rows longer than 64 blocks, whose block scales take registers:
+// four rows of them drop the grouped SwiGLU GEMV of the MoE layer to two
+// waves per SIMD, while the row-scaled formats keep three and gain).
 // Small per-wave work and many waves keep the most loads in flight per CU.
-int pick_rows(int epi, int pro, int M, int64_t k, int64_t units) {
+int pick_rows(int epi, int pro, int M, int64_t k, int64_t units, int fmt = FMT_Q4_0) {
     const int P = rows_per_unit(epi);
-    const int cap = (M <= 2 && k / QBLK <= WAVE) ? 4 : 2;   // long rows hold more registers
+    const int cap = (M <= 2 && (k / QBLK <= WAVE || fmt != FMT_Q4_0)) ? 4 : 2;
     int upw = units > 2 * 8192 ? 4 : (units > 8192 ? 2 : 1);
     if (pro == PRO_RMSNORM && epi == EPI_SWIGLU && units >= 2048) upw = std::max(upw, 2);
     while (upw * P > cap) upw /= 2;
@@ -635,7 +637,7 @@ void launch_cfg(const GemvArgs& a, hipStream_t s) {
 template <int FMT, int M, int U, int EPI, int PRO, int KC, bool KLOOP>
 void launch_r(const GemvArgs& a, hipStream_t s) {
     constexpr int P = rows_per_unit(EPI);
-    const int R = pick_rows(EPI, PRO, M, a.k, units_of(a, EPI) * a.groups);
+    const int R = pick_rows(EPI, PRO, M, a.k, units_of(a, EPI) * a.groups, FMT);
     if constexpr (M <= 2) {
         if (R >= 4) { launch_cfg<FMT, M, 4, U, EPI, PRO, KC, KLOOP>(a, s); return; }
     }
