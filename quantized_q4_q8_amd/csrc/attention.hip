@@ -4,11 +4,13 @@
 // V with a KV cache), TinyLLaMA-in-C++ guide 4.3 (several query heads share
 // one KV head) and 7 (attend over cache rows 0..N).
 //
-// Split over the context in two passes.  The chunk pass reads each 64-row
-// chunk of a KV head once for all query heads of its group and writes one
-// record per (head, chunk); the merge pass combines a head's records by
-// log-sum-exp rescaling.  The kernel boundary between them is the cheapest
-// way to make the records of every die visible to the merging workgroup.
+// Few tokens (decode): split over the context in two passes.  The chunk
+// pass reads each 64-row chunk of a KV head once for all query heads of its
+// group and writes one record per (head, chunk); the merge pass combines a
+// head's records by log-sum-exp rescaling.  The kernel boundary between them
+// is the cheapest way to make the records of every die visible to the
+// merging workgroup.  Many tokens (prefill): one pass over the chunks with
+// an online softmax, its two products on the fp64 matrix cores.
 // Scores, softmax and the weighted sums are fp64 and the output is rounded
 // once to fp32.
 #include "internal.h"
@@ -235,163 +237,188 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     }
 }
 
-// Many-token pass (prefill): workgroup (tile of TQ consecutive tokens, KV
-// head g) walks the KV chunks once for all tokens and all query heads of
-// the group, keeping a running (max, sum, output) per (token, head) row and
-// rescaling it as each chunk's scores arrive (the online form of the
-// max-subtracted softmax); nothing is written between chunks.  A tile is
-// processed in runs of consecutive tokens of the same sequence.  Wave w
-// takes query heads w, w + 8; lane = key for the scores, lane = output
-// dimension for the weighted sum.  fp64 throughout, K/V widened in LDS.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// Attention for many tokens on the fp64 matrix cores (v_mfma_f64_16x16x4f64).
+// Same result as the online softmax above: per (token, head) row the scores
+// of each 64-key chunk are s = q.k / sqrt(hd) in fp64, the running max,
+// sum and output are rescaled by exp(m_old - m_new), and the output is
+// o / l rounded once.  Layout of one 16x16x4 product (wave64): A[i][k] in
+// lane i + 16k, B[k][j] in lane j + 16k, C[i][j] in lane j + 16 (i % 4),
+// register i / 4.
+// A workgroup (4 waves) takes 64 query rows = (64 / G) tokens x the G query
+// heads of one KV head; wave w owns rows 16w .. 16w + 15, and lane l works on
+// row 16w + l % 16.  The scores are formed transposed, S^T = K Q^T (A = K
+// from LDS, B = Q^T from registers), so that each lane's C registers are
+// exactly the B operand of O^T = V^T P^T (register v of key tile kt is key
+// step 4 kt + v): the probabilities never leave registers.  K and V are
+// staged in LDS as fp32 (exact widenings of fp16) with row strides HD + 2
+// and HD + 16, which keep the operand reads free of bank conflicts.
 template <int HD>
-__global__ __launch_bounds__(512) void k_attn_flash(
+__global__ __launch_bounds__(256) void k_attn_flash_mfma(
     const float* __restrict__ q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, float* __restrict__ out,
     int64_t o_ts, int8_t* __restrict__ oq, uint16_t* __restrict__ od) {
-    constexpr int TQ = 8;               // tokens per tile
-    constexpr int NW = 8;               // waves per workgroup
-    constexpr int MAXG = 512 / HD;      // query heads per group at most
-    constexpr int HPW = MAXG / NW;      // query heads per wave at most
-    __shared__ __align__(16) double qs[TQ][MAXG * HD];
-    __shared__ float ks[ACH][HD + 1];
-    __shared__ __align__(16) float vs[ACH][HD];
-    __shared__ __align__(16) double ps[NW][TQ][ACH];
+    constexpr int NS = HD / 4;     // k-steps of the score product (dims)
+    constexpr int NDT = HD / 16;   // dim tiles of the output
+    constexpr int KS = HD + 2, VS = HD + 16;
+    __shared__ float ks[ACH][KS];
+    __shared__ float vs[ACH][VS];
 
-    const int64_t g = blockIdx.y, t0 = (int64_t)blockIdx.x * TQ;
     const int G = (int)(nq / nkv);
+    const int TQ = 64 / G;   // tokens per workgroup
+    const int64_t g = blockIdx.y, t0 = (int64_t)blockIdx.x * TQ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ntile = (int)min((int64_t)TQ, tokens - t0);
+    const int qr = 16 * wave + (lane & 15);            // this lane's query row
+    const int qi = qr / G, qh = qr % G;                // its token and head
+    const bool qvalid = qr < TQ * G && qi < ntile;
+    const int kq = lane >> 4;                          // lane's k index (0..3)
     const double rscale = sqrt((double)HD);
 
     for (int i0 = 0; i0 < ntile;) {   // runs of one sequence (uniform)
         const int s0 = seq[t0 + i0];
         int i1 = i0 + 1;
         while (i1 < ntile && seq[t0 + i1] == s0) ++i1;
-        const int nrun = i1 - i0;
-        int pi[TQ];
+        // row limits: the last ring row attended (-1: nothing)
         int kmax = -1;
+        for (int i = i0; i < i1; ++i) {
+            const int p = pos[t0 + i];
+            if (p >= 0) kmax = max(kmax, (int)min((int64_t)p, cap - 1));
+        }
+        const bool mine = qvalid && qi >= i0 && qi < i1;
+        int pl = -1;
+        if (mine) {
+            const int p = pos[t0 + qi];
+            pl = p >= 0 ? (int)min((int64_t)p, cap - 1) : -1;
+        }
+        double qT[NS];
 #pragma unroll
-        for (int i = 0; i < TQ; ++i) {
-            pi[i] = -1;
-            if (i < nrun) {
-                const int p = pos[t0 + i0 + i];
-                if (p >= 0) {   // negative positions attend to nothing
-                    pi[i] = (int)min((int64_t)p, cap - 1);   // last ring row attended
-                    kmax = max(kmax, pi[i]);
-                }
-            }
-        }
-        __syncthreads();   // the previous run is done with qs
-        for (int idx = tid; idx < nrun * G * HD; idx += 512) {
-            const int i = idx / (G * HD), r = idx % (G * HD);
-            qs[i][r] = (double)q[(t0 + i0 + i) * q_ts + g * G * HD + r];
-        }
+        for (int st = 0; st < NS; ++st)
+            qT[st] = mine ? (double)q[(t0 + qi) * q_ts + (g * G + qh) * HD + 4 * st + kq] : 0.0;
 
-        double m[HPW][TQ], l[HPW][TQ], o[HPW][TQ];
+        double m = -INFINITY, lsum = 0.0;
+        v4d o[NDT];
 #pragma unroll
-        for (int hp = 0; hp < HPW; ++hp)
-#pragma unroll
-            for (int i = 0; i < TQ; ++i) {
-                m[hp][i] = -INFINITY;
-                l[hp][i] = 0.0;
-                o[hp][i] = 0.0;
-            }
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = v4d{0.0, 0.0, 0.0, 0.0};
 
         const int64_t cbase = (((int64_t)s0 * nkv + g) * cap) * HD;
         for (int c = 0; c * ACH <= kmax; ++c) {
-            const int64_t r0 = (int64_t)c * ACH;
-            __syncthreads();   // ks/vs (and qs, first time) ready for rewriting / reading
-            for (int i = tid; i < ACH * HD / 8; i += 512) {
+            const int r0 = c * ACH;
+            __syncthreads();   // the previous chunk's operand reads are done
+            for (int i = tid; i < ACH * HD / 8; i += 256) {
                 const int r = (i * 8) / HD, d = (i * 8) % HD;
                 uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
                 if (r0 + r <= kmax) {
-                    kv = *reinterpret_cast<const uint4*>(kc + cbase + (r0 + r) * HD + d);
-                    vv = *reinterpret_cast<const uint4*>(vc + cbase + (r0 + r) * HD + d);
+                    kv = *reinterpret_cast<const uint4*>(kc + cbase + (int64_t)(r0 + r) * HD + d);
+                    vv = *reinterpret_cast<const uint4*>(vc + cbase + (int64_t)(r0 + r) * HD + d);
                 }
                 const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    ks[r][d + 2 * e] = h2f((uint16_t)(kw[e] & 0xFFFF));
-                    ks[r][d + 2 * e + 1] = h2f((uint16_t)(kw[e] >> 16));
-                    vs[r][d + 2 * e] = h2f((uint16_t)(vw[e] & 0xFFFF));
-                    vs[r][d + 2 * e + 1] = h2f((uint16_t)(vw[e] >> 16));
+                    *reinterpret_cast<float2*>(&ks[r][d + 2 * e]) =
+                        make_float2(h2f((uint16_t)(kw[e] & 0xFFFF)), h2f((uint16_t)(kw[e] >> 16)));
+                    *reinterpret_cast<float2*>(&vs[r][d + 2 * e]) =
+                        make_float2(h2f((uint16_t)(vw[e] & 0xFFFF)), h2f((uint16_t)(vw[e] >> 16)));
                 }
             }
             __syncthreads();
+
+            // S^T for 4 key tiles: C[key][row], key = 16 kt + 4 v + kq
+            v4d sc[4];
 #pragma unroll
-            for (int hp = 0; hp < HPW; ++hp) {
-                const int hh = wave + hp * NW;
-                if (hh >= G) break;   // uniform over the wave
-                // scores of key r0 + lane for the run's tokens
-                double sc[TQ];
+            for (int kt = 0; kt < 4; ++kt) sc[kt] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-                for (int i = 0; i < TQ; ++i) sc[i] = 0.0;
-#pragma unroll 4
-                for (int d = 0; d < HD; d += 2) {
-                    const double k0 = (double)ks[lane][d], k1 = (double)ks[lane][d + 1];
+            for (int st = 0; st < NS; ++st) {
 #pragma unroll
-                    for (int i = 0; i < TQ; ++i) {
-                        const double2 qq = *reinterpret_cast<const double2*>(&qs[i][hh * HD + d]);
-                        sc[i] = fma(qq.x, k0, sc[i]);
-                        sc[i] = fma(qq.y, k1, sc[i]);
-                    }
+                for (int kt = 0; kt < 4; ++kt) {
+                    const double a = (double)ks[16 * kt + (lane & 15)][4 * st + kq];
+                    sc[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qT[st], sc[kt], 0, 0, 0);
                 }
-                const int key = (int)r0 + lane;
-#pragma unroll
-                for (int i = 0; i < TQ; ++i) {
-                    const bool ok = key <= pi[i];   // pi = -1 for absent or out-of-range tokens
-                    const double s = ok ? sc[i] / rscale : -INFINITY;
-                    const double cm = group_max<WAVE>(s);
-                    double pv = 0.0;
-                    if (cm != -INFINITY) {   // uniform over the wave
-                        const double mn = fmax(m[hp][i], cm);
-                        const double f = exp(m[hp][i] - mn);   // 0 when m was -inf
-                        pv = ok ? exp(s - mn) : 0.0;
-                        l[hp][i] = fma(l[hp][i], f, group_sum<WAVE>(pv));
-                        o[hp][i] *= f;
-                        m[hp][i] = mn;
-                    }
-                    ps[wave][i][lane] = pv;
-                }
-                __builtin_amdgcn_wave_barrier();
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (lane < HD) {   // weighted values, lane = dimension
-#pragma unroll 4
-                    for (int j = 0; j < ACH; j += 2) {
-                        const double v0 = (double)vs[j][lane], v1 = (double)vs[j + 1][lane];
-#pragma unroll
-                        for (int i = 0; i < TQ; ++i) {
-                            const double2 pp = *reinterpret_cast<const double2*>(&ps[wave][i][j]);
-                            o[hp][i] = fma(pp.x, v0, o[hp][i]);
-                            o[hp][i] = fma(pp.y, v1, o[hp][i]);
-                        }
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();   // ps is rewritten next
             }
+            // mask, scale and the chunk's row max (the row's 64 keys sit in
+            // this lane's 16 registers and lanes l ^ 16, l ^ 32, l ^ 48)
+            double cm = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int key = r0 + 16 * kt + 4 * v + kq;
+                    const double sv = key <= pl ? sc[kt][v] / rscale : -INFINITY;
+                    sc[kt][v] = sv;
+                    cm = fmax(cm, sv);
+                }
+            cm = fmax(cm, __shfl_xor(cm, 16, WAVE));
+            cm = fmax(cm, __shfl_xor(cm, 32, WAVE));
+            const bool live = cm != -INFINITY;
+            const double mn = live ? fmax(m, cm) : m;
+            const double f = live ? exp(m - mn) : 1.0;   // 0 when m was -inf
+            double rs = 0.0;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const double pv = sc[kt][v] != -INFINITY ? exp(sc[kt][v] - mn) : 0.0;
+                    sc[kt][v] = pv;
+                    rs += pv;
+                }
+            rs += __shfl_xor(rs, 16, WAVE);
+            rs += __shfl_xor(rs, 32, WAVE);
+            if (live) {
+                lsum = fma(lsum, f, rs);
+                m = mn;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
+            }
+            // O^T += V^T P^T: key step 4 kt + v takes register v of tile kt
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const double a = (double)vs[16 * kt + 4 * v + kq][16 * dt + (lane & 15)];
+                        o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, sc[kt][v], o[dt], 0, 0, 0);
+                    }
         }
 
-        // outputs of the run: fp32 and/or Q8_0 (one 32-lane group per block)
+        // outputs of the run: this lane holds dims 16 dt + 4 v + kq of its row
+        float ov[NDT][4];
 #pragma unroll
-        for (int hp = 0; hp < HPW; ++hp) {
-            const int hh = wave + hp * NW;
-            if (hh >= G) break;
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < TQ; ++i) {
-                if (i >= nrun) break;
-                const float v = l[hp][i] > 0.0 ? (float)(o[hp][i] / l[hp][i]) : 0.0f;
-                const int64_t col = (t0 + i0 + i) * o_ts + (g * G + hh) * HD;
-                if (lane < HD) {
-                    if (out) out[col + lane] = v;
-                    if (oq) {
-                        const float amax = group_max<QBLK>(fabsf(v));
-                        const float d = amax / 127.0f;
-                        int qv = 0;
-                        if (d != 0.0f) qv = (int)fminf(127.0f, fmaxf(-127.0f, roundf(v / d)));
-                        oq[col + lane] = (int8_t)qv;
-                        if ((lane & (QBLK - 1)) == 0) od[(col + lane) / QBLK] = f2h(d);
-                    }
+            for (int v = 0; v < 4; ++v) ov[dt][v] = lsum > 0.0 ? (float)(o[dt][v] / lsum) : 0.0f;
+        const int64_t col = (t0 + qi) * o_ts + (g * G + qh) * HD;
+        if (out && mine) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) out[col + 16 * dt + 4 * v + kq] = ov[dt][v];
+        }
+        if (oq) {
+            // Q8_0 block b of the row: dim tiles 2b, 2b + 1 over the four
+            // lanes of the row
+#pragma unroll
+            for (int b = 0; b < HD / QBLK; ++b) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int dt = 2 * b; dt < 2 * b + 2; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(ov[dt][v]));
+                amax = fmaxf(amax, __shfl_xor(amax, 16, WAVE));
+                amax = fmaxf(amax, __shfl_xor(amax, 32, WAVE));
+                const float d = amax / 127.0f;
+                if (mine) {
+#pragma unroll
+                    for (int dt = 2 * b; dt < 2 * b + 2; ++dt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            int qv = 0;
+                            if (d != 0.0f) qv = (int)fminf(127.0f, fmaxf(-127.0f, roundf(ov[dt][v] / d)));
+                            oq[col + 16 * dt + 4 * v + kq] = (int8_t)qv;
+                        }
+                    if (kq == 0) od[(col + b * QBLK) / QBLK] = f2h(d);
                 }
             }
         }
@@ -408,13 +435,14 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     const int64_t nch = (cap + ACH - 1) / ACH;
     if (nch > MAX_CHUNKS || (nq / nkv) * hd > 512) return QK_ESHAPE;
     if (tokens > FLASH_MIN_TOKENS) {
-        dim3 fgrid((unsigned)((tokens + 7) / 8), (unsigned)nkv);
+        const int64_t tq = 64 / (nq / nkv);   // tokens per workgroup of the matrix-core pass
+        dim3 fgrid((unsigned)((tokens + tq - 1) / tq), (unsigned)nkv);
         if (hd == 32)
-            hipLaunchKernelGGL(k_attn_flash<32>, fgrid, dim3(512), 0, s, q, q_ts, tokens, nq, nkv, kc,
-                               vc, cap, pos, seq, out, o_ts, oq, od);
+            hipLaunchKernelGGL(k_attn_flash_mfma<32>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
+                               kc, vc, cap, pos, seq, out, o_ts, oq, od);
         else if (hd == 64)
-            hipLaunchKernelGGL(k_attn_flash<64>, fgrid, dim3(512), 0, s, q, q_ts, tokens, nq, nkv, kc,
-                               vc, cap, pos, seq, out, o_ts, oq, od);
+            hipLaunchKernelGGL(k_attn_flash_mfma<64>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
+                               kc, vc, cap, pos, seq, out, o_ts, oq, od);
         else
             return QK_ESHAPE;
         return qk_launch_status();
