@@ -7,15 +7,19 @@
 // block dot of a 32 x 32 tile of (token, weight row) pairs; the two scales
 // are applied right after it and the scaled block dots are summed in fp64.
 //
-// Tile: a workgroup (4 waves) computes 128 tokens x 128 weight rows; each
-// wave 64 x 64 as 2 x 2 MFMA tiles.  Activations are the MFMA's A operand
-// (rows = tokens) and weights the B operand (columns = weight rows), so in
-// the 32 x 32 accumulator a lane owns one weight row and 16 tokens and the
-// stores of a register are 32 consecutive floats of one output row.
+// Tile: a workgroup (4 waves) computes 64 tokens x 128 weight rows; each
+// wave 32 tokens x 64 rows as two MFMA tiles (two workgroups share a CU).  Activations are the MFMA's A
+// operand (rows = tokens) and weights the B operand (columns = weight rows),
+// so in the 32 x 32 accumulator a lane owns one weight row and 16 tokens and
+// the stores of a register are 32 consecutive floats of one output row.
 // KB = 4 blocks (K = 128) are staged in LDS per step, double-buffered so the
-// global loads of step s + 1 are in flight during the MFMAs of step s.
-// Nibbles become signed int8 codes in registers: (c + 0x78) ^ 0x80 maps
-// c in [0, 15] to c - 8 in two's complement with no carry between bytes.
+// global loads of step s + 1 are in flight during the MFMAs of step s.  The
+// weight nibbles become signed int8 codes once, while they are staged
+// ((c + 0x78) ^ 0x80 maps c in [0, 15] to c - 8 with no carry between
+// bytes), so every wave reads ready MFMA operands.  The activation scales
+// are staged as fp64, which makes each scaled block sum
+// fma(isum * dx, dw, acc): isum * dx is exact in fp64 (15 + 11 bits) and the
+// fma rounds the exact triple product once.
 #include "internal.h"
 
 namespace qk {
@@ -25,16 +29,20 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BT = 128;  // tokens per workgroup
+constexpr int BT = 64;   // tokens per workgroup
 constexpr int BR = 128;  // weight rows per workgroup (physical)
 constexpr int KB = 4;    // blocks per LDS stage
-constexpr int A_STRIDE = KB * QBLK + 16;   // bytes per token row in LDS (padded)
-constexpr int B_STRIDE = KB * 16 + 16;     // bytes per weight row in LDS (padded)
+constexpr int NT = 256;  // threads per workgroup: 4 waves, 2 (tokens) x 2 (rows)
+constexpr int STRIDE = KB * QBLK + 16;   // bytes per token / weight row in LDS (padded)
+constexpr int A_PER = BT * KB * 2 / NT;  // 16-byte activation chunks per thread and step
+constexpr int B_PER = BR * KB / NT;      // 16-byte weight chunks per thread and step
+constexpr int DB_PER = BR * KB / NT;     // weight scales per thread and step
+static_assert(BT * KB == NT, "one activation scale per thread and step");
 
 struct __align__(16) Stage {
-    uint8_t a[BT * A_STRIDE];   // activation codes
-    uint8_t b[BR * B_STRIDE];   // weight nibbles
-    float da[KB][BT];           // activation scales
+    int8_t a[BT * STRIDE];      // activation codes
+    int8_t b[BR * STRIDE];      // weight codes (signed int8)
+    double da[KB][BT];          // activation scales
     float db[KB][BR];           // weight scales
 };
 
@@ -44,10 +52,18 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
     return (float)(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
+__device__ __forceinline__ uint4 nib_codes(const uint4 v, int sh) {
+    const uint32_t m4 = 0x0F0F0F0Fu;
+    return make_uint4((((v.x >> sh) & m4) + 0x78787878u) ^ 0x80808080u,
+                      (((v.y >> sh) & m4) + 0x78787878u) ^ 0x80808080u,
+                      (((v.z >> sh) & m4) + 0x78787878u) ^ 0x80808080u,
+                      (((v.w >> sh) & m4) + 0x78787878u) ^ 0x80808080u);
+}
+
 }  // namespace
 
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     __shared__ Stage st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,13 +88,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
         return c0 + pr < nphys;
     };
 
-    // ---- global -> register staging (per thread: 4 A chunks, 2 B chunks, 2+2 scales)
-    uint4 ra[4], rb[2];
-    float rda[2], rdb[2];
+    // ---- global -> register staging (per thread and step: A_PER activation
+    // chunks, B_PER weight chunks, one activation scale, DB_PER weight scales)
+    uint4 ra[A_PER], rb[B_PER];
+    float rda, rdb[DB_PER];
     auto gload = [&](int64_t kb0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i;         // 1024 chunks of 16 B: [token][KB*2]
+        for (int i = 0; i < A_PER; ++i) {
+            const int idx = tid + NT * i;          // chunks of 16 B: [token][KB*2]
             const int tr = idx >> 3, part = idx & 7;
             const int64_t t = t0 + tr;
             const int64_t b = kb0 + (part >> 1);
@@ -88,8 +105,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
                 ra[i] = make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;         // 512 chunks: [row][KB]
+        for (int i = 0; i < B_PER; ++i) {
+            const int idx = tid + NT * i;          // chunks of 16 B: [row][KB]
             const int pr = idx >> 2, bb = idx & 3;
             const int64_t b = kb0 + bb;
             if (prow_valid(pr) && b < nb)
@@ -97,51 +114,56 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
             else
                 rb[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;         // 512 scales: [KB][128]
-            const int bb = idx >> 7, r = idx & 127;
+        {
+            const int bb = tid / BT, r = tid % BT;   // activation scales [KB][BT]
             const int64_t b = kb0 + bb;
             const int64_t t = t0 + r;
-            rda[i] = (t < m && b < nb) ? h2f(a.xd[t * nb + b]) : 0.0f;
+            rda = (t < m && b < nb) ? h2f(a.xd[t * nb + b]) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < DB_PER; ++i) {
+            const int idx = tid + NT * i;            // weight scales [KB][BR]
+            const int bb = idx / BR, r = idx % BR;
+            const int64_t b = kb0 + bb;
             rdb[i] = (prow_valid(r) && b < nb) ? h2f(a.wd[prow_of(r) * nb + b]) : 0.0f;
         }
     };
     auto sstore = [&](Stage& s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i;
+        for (int i = 0; i < A_PER; ++i) {
+            const int idx = tid + NT * i;
             const int tr = idx >> 3, part = idx & 7;
-            *reinterpret_cast<uint4*>(s.a + tr * A_STRIDE + part * 16) = ra[i];
+            *reinterpret_cast<uint4*>(s.a + tr * STRIDE + part * 16) = ra[i];
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;
+        for (int i = 0; i < B_PER; ++i) {
+            // block bb of row pr: elements 0..15 from the low nibbles, 16..31
+            // from the high ones
+            const int idx = tid + NT * i;
             const int pr = idx >> 2, bb = idx & 3;
-            *reinterpret_cast<uint4*>(s.b + pr * B_STRIDE + bb * 16) = rb[i];
+            *reinterpret_cast<uint4*>(s.b + pr * STRIDE + bb * QBLK) = nib_codes(rb[i], 0);
+            *reinterpret_cast<uint4*>(s.b + pr * STRIDE + bb * QBLK + 16) = nib_codes(rb[i], 4);
         }
+        s.da[tid / BT][tid % BT] = (double)rda;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;
-            const int bb = idx >> 7, r = idx & 127;
-            s.da[bb][r] = rda[i];
-            s.db[bb][r] = rdb[i];
+        for (int i = 0; i < DB_PER; ++i) {
+            const int idx = tid + NT * i;
+            s.db[idx / BR][idx % BR] = rdb[i];
         }
     };
 
-    double acc[2][2][16];
+    double acc[2][16];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0;
+        for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0;
 
     // LDS row (weights) of column tile cb for this wave
     auto lds_col = [&](int cb) -> int {
         if (EPI == EPI_SWIGLU) return cb * (BR / 2) + wc * 32 + j;  // cb 0: gate, 1: up
         return wc * 64 + cb * 32 + j;
     };
+    const int tra = wt * 32 + j;   // activation row (token) of this lane's A operand
 
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const int64_t nsteps = (nb + KB - 1) / KB;
@@ -153,72 +175,54 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemvArgs a) {
         if (s + 1 < nsteps) gload((s + 1) * KB);
 #pragma unroll 1
         for (int bb = 0; bb < KB; ++bb) {
-            v4i xa[2], wb[2];
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta) {
-                const int tr = wt * 64 + ta * 32 + j;
-                const uint4 v = *reinterpret_cast<const uint4*>(cur.a + tr * A_STRIDE + bb * QBLK + h * 16);
-                xa[ta] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-            }
+            const uint4 av = *reinterpret_cast<const uint4*>(cur.a + tra * STRIDE + bb * QBLK + h * 16);
+            const v4i xa = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+            v16i isum[2];
+            double dw[2];
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const uint4 v = *reinterpret_cast<const uint4*>(cur.b + lds_col(cb) * B_STRIDE + bb * 16);
-                const uint32_t m4 = 0x0F0F0F0Fu;
-                const int sh = 4 * h;  // lane half 0: elements 0..15 (low nibbles), 1: 16..31
-                uint32_t c[4] = {(v.x >> sh) & m4, (v.y >> sh) & m4, (v.z >> sh) & m4, (v.w >> sh) & m4};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) c[q] = (c[q] + 0x78787878u) ^ 0x80808080u;
-                wb[cb] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+                const uint4 bv = *reinterpret_cast<const uint4*>(cur.b + lds_col(cb) * STRIDE + bb * QBLK + h * 16);
+                isum[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, v4i{(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w},
+                                                                 zero, 0, 0, 0);
+                dw[cb] = (double)cur.db[bb][lds_col(cb)];
             }
-            float dwl[2];
+            // register v is token row 8 (v / 4) + 4 h + (v % 4) of the wave's 32
+            double dx[16];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) dwl[cb] = cur.db[bb][lds_col(cb)];
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta) {
-                float dxa[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(
-                        &cur.da[bb][wt * 64 + ta * 32 + 8 * q + 4 * h]);
-                    dxa[4 * q] = d4.x; dxa[4 * q + 1] = d4.y; dxa[4 * q + 2] = d4.z; dxa[4 * q + 3] = d4.w;
-                }
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const v16i isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[ta], wb[cb], zero, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)   // scale product exact in fp32, term exact in fp64
-                        acc[ta][cb][v] = fma((double)(dxa[v] * dwl[cb]), (double)isum[v], acc[ta][cb][v]);
-                }
+            for (int q = 0; q < 4; ++q) {
+                const double2 d0 = *reinterpret_cast<const double2*>(&cur.da[bb][wt * 32 + 8 * q + 4 * h]);
+                const double2 d1 = *reinterpret_cast<const double2*>(&cur.da[bb][wt * 32 + 8 * q + 4 * h + 2]);
+                dx[4 * q] = d0.x; dx[4 * q + 1] = d0.y; dx[4 * q + 2] = d1.x; dx[4 * q + 3] = d1.y;
             }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[cb][v] = fma((double)isum[cb][v] * dx[v], dw[cb], acc[cb][v]);
         }
-        if (s + 1 < nsteps) {
-            sstore(st[(s + 1) & 1]);
-        }
+        if (s + 1 < nsteps) sstore(st[(s + 1) & 1]);
         __syncthreads();
     }
 
-    // ---- epilogue: lane j owns weight column lds_col(cb); register v is token
-    // row 8 * (v / 4) + 4 * h + (v % 4) of the 32-token tile.
+    // ---- epilogue: lane j owns weight column lds_col(cb); register v is
+    // token row 8 * (v / 4) + 4 * h + (v % 4) of the wave's 32-token tile.
 #pragma unroll
-    for (int ta = 0; ta < 2; ++ta) {
+    for (int v = 0; v < 16; ++v) {
+        const int64_t t = t0 + wt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+        if (t >= m) continue;
+        if (EPI == EPI_STORE) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t t = t0 + wt * 64 + ta * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-            if (t >= m) continue;
-            if (EPI == EPI_STORE) {
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const int pr = lds_col(cb);
-                    if (!prow_valid(pr)) continue;
-                    const int64_t r = prow_of(pr);
-                    float val = (float)acc[ta][cb][v];
-                    if (a.residual) val = a.residual[t * a.ldr + r] + val;
-                    a.y[t * a.ldy + r] = val;
-                }
-            } else {
-                const int64_t f = c0 + wc * 32 + j;
-                if (f < a.ffn) a.y[t * a.ldy + f] = swiglu1((float)acc[ta][0][v], (float)acc[ta][1][v]);
+            for (int cb = 0; cb < 2; ++cb) {
+                const int pr = lds_col(cb);
+                if (!prow_valid(pr)) continue;
+                const int64_t r = prow_of(pr);
+                float val = (float)acc[cb][v];
+                if (a.residual) val = a.residual[t * a.ldr + r] + val;
+                a.y[t * a.ldy + r] = val;
             }
+        } else {
+            const int64_t f = c0 + wc * 32 + j;
+            if (f < a.ffn) a.y[t * a.ldy + f] = swiglu1((float)acc[0][v], (float)acc[1][v]);
         }
     }
 }
@@ -227,10 +231,10 @@ int launch_gemm(const GemvArgs& a, int epi, hipStream_t s) {
     const unsigned gt = (unsigned)((a.m + BT - 1) / BT);
     if (epi == EPI_SWIGLU) {
         dim3 grid((unsigned)((a.ffn + BR / 2 - 1) / (BR / 2)), gt);
-        hipLaunchKernelGGL(k_gemm_mfma<EPI_SWIGLU>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gemm_mfma<EPI_SWIGLU>, grid, dim3(NT), 0, s, a);
     } else {
         dim3 grid((unsigned)((a.n + BR - 1) / BR), gt);
-        hipLaunchKernelGGL(k_gemm_mfma<EPI_STORE>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gemm_mfma<EPI_STORE>, grid, dim3(NT), 0, s, a);
     }
     return qk_launch_status();
 }
