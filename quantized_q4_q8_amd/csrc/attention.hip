@@ -253,7 +253,9 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 // exactly the B operand of O^T = V^T P^T (register v of key tile kt is key
 // step 4 kt + v): the probabilities never leave registers.  K and V are
 // staged in LDS as fp32 (exact widenings of fp16) with row strides HD + 2
-// and HD + 16, which keep the operand reads free of bank conflicts.
+// and HD + 16, which keep the operand reads free of bank conflicts, and
+// double-buffered: the next chunk's rows are loaded into registers while
+// the current one is multiplied.
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_flash_mfma(
     const float* __restrict__ q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
@@ -263,8 +265,9 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
     constexpr int NS = HD / 4;     // k-steps of the score product (dims)
     constexpr int NDT = HD / 16;   // dim tiles of the output
     constexpr int KS = HD + 2, VS = HD + 16;
-    __shared__ float ks[ACH][KS];
-    __shared__ float vs[ACH][VS];
+    constexpr int KVPER = ACH * HD / 8 / 256;   // 8-value chunks of K (and of V) per thread
+    __shared__ float ks[2][ACH][KS];
+    __shared__ float vs[2][ACH][VS];
 
     const int G = (int)(nq / nkv);
     const int TQ = 64 / G;   // tokens per workgroup
@@ -304,26 +307,47 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
         for (int dt = 0; dt < NDT; ++dt) o[dt] = v4d{0.0, 0.0, 0.0, 0.0};
 
         const int64_t cbase = (((int64_t)s0 * nkv + g) * cap) * HD;
-        for (int c = 0; c * ACH <= kmax; ++c) {
-            const int r0 = c * ACH;
-            __syncthreads();   // the previous chunk's operand reads are done
-            for (int i = tid; i < ACH * HD / 8; i += 256) {
-                const int r = (i * 8) / HD, d = (i * 8) % HD;
-                uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-                if (r0 + r <= kmax) {
-                    kv = *reinterpret_cast<const uint4*>(kc + cbase + (int64_t)(r0 + r) * HD + d);
-                    vv = *reinterpret_cast<const uint4*>(vc + cbase + (int64_t)(r0 + r) * HD + d);
-                }
-                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+        uint4 pk[KVPER], pv[KVPER];   // rows of the next chunk, in flight
+        auto gload_kv = [&](int r0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<float2*>(&ks[r][d + 2 * e]) =
-                        make_float2(h2f((uint16_t)(kw[e] & 0xFFFF)), h2f((uint16_t)(kw[e] >> 16)));
-                    *reinterpret_cast<float2*>(&vs[r][d + 2 * e]) =
-                        make_float2(h2f((uint16_t)(vw[e] & 0xFFFF)), h2f((uint16_t)(vw[e] >> 16)));
+            for (int e = 0; e < KVPER; ++e) {
+                const int i = tid + 256 * e;
+                const int r = (i * 8) / HD, d = (i * 8) % HD;
+                pk[e] = make_uint4(0, 0, 0, 0);
+                pv[e] = make_uint4(0, 0, 0, 0);
+                if (r0 + r <= kmax) {
+                    pk[e] = *reinterpret_cast<const uint4*>(kc + cbase + (int64_t)(r0 + r) * HD + d);
+                    pv[e] = *reinterpret_cast<const uint4*>(vc + cbase + (int64_t)(r0 + r) * HD + d);
                 }
             }
+        };
+        auto sstore_kv = [&](int buf) {
+#pragma unroll
+            for (int e = 0; e < KVPER; ++e) {
+                const int i = tid + 256 * e;
+                const int r = (i * 8) / HD, d = (i * 8) % HD;
+                const uint32_t kw[4] = {pk[e].x, pk[e].y, pk[e].z, pk[e].w};
+                const uint32_t vw[4] = {pv[e].x, pv[e].y, pv[e].z, pv[e].w};
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    *reinterpret_cast<float2*>(&ks[buf][r][d + 2 * f]) =
+                        make_float2(h2f((uint16_t)(kw[f] & 0xFFFF)), h2f((uint16_t)(kw[f] >> 16)));
+                    *reinterpret_cast<float2*>(&vs[buf][r][d + 2 * f]) =
+                        make_float2(h2f((uint16_t)(vw[f] & 0xFFFF)), h2f((uint16_t)(vw[f] >> 16)));
+                }
+            }
+        };
+        if (kmax >= 0) {
+            __syncthreads();   // the previous run is done with both buffers
+            gload_kv(0);
+            sstore_kv(0);
             __syncthreads();
+        }
+        for (int c = 0; c * ACH <= kmax; ++c) {
+            const int r0 = c * ACH;
+            const int cur = c & 1;
+            const bool more = (c + 1) * ACH <= kmax;   // uniform
+            if (more) gload_kv(r0 + ACH);
 
             // S^T for 4 key tiles: C[key][row], key = 16 kt + 4 v + kq
             v4d sc[4];
@@ -333,7 +357,7 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
             for (int st = 0; st < NS; ++st) {
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    const double a = (double)ks[16 * kt + (lane & 15)][4 * st + kq];
+                    const double a = (double)ks[cur][16 * kt + (lane & 15)][4 * st + kq];
                     sc[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qT[st], sc[kt], 0, 0, 0);
                 }
             }
@@ -378,9 +402,11 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
                 for (int v = 0; v < 4; ++v)
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        const double a = (double)vs[16 * kt + 4 * v + kq][16 * dt + (lane & 15)];
+                        const double a = (double)vs[cur][16 * kt + 4 * v + kq][16 * dt + (lane & 15)];
                         o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, sc[kt][v], o[dt], 0, 0, 0);
                     }
+            if (more) sstore_kv(cur ^ 1);   // read two chunks ago, past the last barrier
+            __syncthreads();
         }
 
         // outputs of the run: this lane holds dims 16 dt + 4 v + kq of its row
