@@ -110,6 +110,38 @@ def test_decode_tinyllama_shape_teacher_forced(gpu_lib):
         assert rel_err(got, want) < LAYER_TOL
 
 
+def test_decode_long_context_ring_teacher_forced(gpu_lib):
+    """22-layer decode past an 8192-row ring cache filled to the brim: every
+    step attends to 8192 positions (rows 0..8191 hold positions p - 8191..p),
+    logits within 1e-2 and greedy tokens matching the oracle."""
+    spec = W.DECODE_LONG
+    g, L, cap, ctx = spec["geometry"], spec["layers"], spec["cap"], spec["context"]
+    say("long-context decode: building the 22-layer model")
+    dec, hm = build(spec, 1)
+    kv = []
+    for li in range(L):
+        kc, vc = W.kv_prefill_f16(spec["seed"], li, g.n_kv_heads, cap, g.head_dim, ctx)
+        dec.k_cache[li].copy_(torch.from_numpy(kc.view(np.int16)))
+        dec.v_cache[li].copy_(torch.from_numpy(vc.view(np.int16)))
+        kv.append((kc.view(np.uint16).copy(), vc.view(np.uint16).copy()))
+    tok = synth.randint(spec["seed"], W.TID_TOKENS, 1, spec["vocab"])
+    seq = np.zeros(1, np.int32)
+    for j in (0, 1, 2):
+        say(f"long-context decode step at position {ctx + j}")
+        p = np.array([ctx + j], np.int32)
+        lo = oracle_forward(hm, tok, p, seq, kv)
+        lg, nx = dec.step(dev(tok), dev(p), dev(seq))
+        torch.cuda.synchronize()
+        assert np.max(np.abs(host(lg) - lo)) <= LOGIT_TOL, f"position {ctx + j}"
+        check_tokens(host(nx), lo)
+        tok = np.argmax(lo, axis=-1).astype(np.int32)
+    # positions 8192..8194 overwrote ring rows 0..2
+    for li in (0, L - 1):
+        got = oracle.f16_to_f32(host(dec.k_cache[li], np.uint16)[0][:, :3])
+        want = oracle.f16_to_f32(kv[li][0][0][:, :3])
+        assert rel_err(got, want) < LAYER_TOL
+
+
 def test_prefill_tinyllama_shape_prefix(gpu_lib):
     """The 4 x 512 causal prefill with full logits; by causality the first 16
     tokens of each sequence must match the oracle's 16-token prefill."""
@@ -175,6 +207,54 @@ def test_moe_full_size_sampled(gpu_lib):
             if r == 0:
                 assert np.array_equal(host(guq[e]), a) and np.array_equal(host(dnd[e], np.uint16), d)
             acc += np.float64(w_o[t, r]) * oracle.moe_expert_ffn(x[t], a, b, c, d)
+        assert rel_err(y_h[t], acc.astype(np.float32)) < LAYER_TOL, f"token {t}"
+        checked += 1
+    assert checked >= 3
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_moe_rowq_full_size_sampled(gpu_lib, bits):
+    """The MoE workload with row-scaled int4 / int2 experts (256 resident,
+    64 tokens, top-8): routing for every token, outputs for sampled tokens."""
+    qk = gpu_lib
+    spec = W.MOE
+    seed, T, H, E, F, k = spec["seed"], spec["tokens"], spec["hidden"], spec["experts"], spec["ffn"], spec["top_k"]
+    say(f"moe rowq{bits}: generating and quantizing 256 experts on the GPU")
+    guq = torch.empty((E, 2 * F, H * bits // 8), dtype=torch.uint8, device="cuda")
+    gur = torch.empty((E, 2 * F), dtype=torch.float32, device="cuda")
+    dnq = torch.empty((E, H, F * bits // 8), dtype=torch.uint8, device="cuda")
+    dnr = torch.empty((E, H), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        gu, dn = W.expert_weights_f32(seed, e, H, F)
+        qk.qk_quantize_rowq(to_device(gu), bits, out_q=guq[e], out_r=gur[e])
+        qk.qk_quantize_rowq(to_device(dn), bits, out_q=dnq[e], out_r=dnr[e])
+    x = synth.normal(seed, W.TID_X, (T, H))
+    wr = synth.normal(seed, W.TID_ROUTER, (H, E), W.WEIGHT_STD)
+    say(f"moe rowq{bits}: GPU layer")
+    y, sg, wg = qk.qk_moe_route_and_apply_rowq(dev(x), dev(wr), k, guq, gur, dnq, dnr, bits)
+    torch.cuda.synchronize()
+    sel_o, w_o, logits = oracle.moe_route(x, wr, k, return_logits=True)
+    sel_g, w_g = host(sg), host(wg)
+    from tests.test_gpu_layer import check_routing
+    check_routing(sel_g, w_g, sel_o, w_o, logits)
+    y_h = host(y)
+    checked = 0
+    for t in (0, 17, 42, 63):
+        if not np.array_equal(sel_g[t], sel_o[t]):
+            continue   # a near tie (checked above): either selection is correct
+        say(f"moe rowq{bits}: oracle token {t}")
+        acc = np.zeros(H, np.float64)
+        for r in range(k):
+            e = int(sel_o[t, r])
+            gu, dn = W.expert_weights_f32(seed, e, H, F)
+            a, b = oracle.quantize_rowq(gu, bits)
+            c, d = oracle.quantize_rowq(dn, bits)
+            if r == 0:
+                assert np.array_equal(host(guq[e]), a) and np.array_equal(host(dnr[e]), d)
+            xq, xd = oracle.quantize_q8_0(x[t:t + 1])
+            gup = oracle.qmatmul_rowq(a, b, xq, xd, bits)[0]
+            hq, hd = oracle.quantize_q8_0(oracle.swiglu(gup[:F], gup[F:])[None])
+            acc += np.float64(w_o[t, r]) * oracle.qmatmul_rowq(c, d, hq, hd, bits)[0]
         assert rel_err(y_h[t], acc.astype(np.float32)) < LAYER_TOL, f"token {t}"
         checked += 1
     assert checked >= 3
