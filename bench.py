@@ -404,6 +404,8 @@ def run_matmul(args):
                      "codec": args.codec,
                      "copies": "1 GiB of distinct weight copies rotated per launch",
                      "parallelism": "single GPU"})
+    if bits:
+        out["data"] = f"synthetic: seeded N(0,0.02) weights quantized to row-scaled int{bits}, N(0,1) activations"
     out["roofline"] = {"bound": "hbm", "kernel": "k_gemv_rowq (M=1, store epilogue)" if bits else "k_gemv (M=1, store epilogue)",
                        "achieved": head["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(head["cold_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
@@ -575,6 +577,8 @@ def run_moe(args):
                     {"workload": "moe layer: hidden 6144, 256 experts x SwiGLU 2048, 64 tokens, top-8",
                      "codec": args.codec, "bytes_per_expert": per_expert,
                      "distinct_experts": distinct, "parallelism": "single GPU"})
+    if bits:
+        out["data"] = f"synthetic: seeded N(0,0.02) weights quantized to row-scaled int{bits}, N(0,1) activations"
     out["us_per_layer"] = round(us, 2)
     out["roofline"] = {"bound": "hbm", "kernel": "whole MoE layer (router, top-k, grouping, grouped GEMVs, combine)",
                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -646,6 +650,18 @@ def run_sample(args):
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(head["GBps"] / HBM_PEAK_GBS, 5),
                        "traffic": None, "bytes_per_launch": V * 4, "avg_us": head["us_per_call"]}
     out["rows"] = rows_out
+    out["data"] = "synthetic: seeded N(0,1) x 2.5 logits, seeded uniforms"
+    if not args.no_cpu_baseline:
+        import oracle
+        x = normal(5, 200, (1, V)) * np.float32(2.5)
+        uh = (randint(5, 300, 1, 1 << 30).astype(np.float64) + 0.5) / (1 << 30)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or n == 0:
+            oracle.sample(x, 40, 0.9, 0.7, uh)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        out["cpu_baseline"] = {"value": round(1.0 / dt, 2), "unit": "calls/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} oracle sampler calls on one 32000-logit row (single-threaded)"}
     print(json.dumps(out), flush=True)
 
 
