@@ -81,7 +81,9 @@ def test_block_dots_bit_exact_on_any_bytes(gpu_lib, n, k, m):
 # ---------------------------------------------------------------- matmul
 MM_CASES = [(5632, 2048, 1), (2048, 5632, 1), (5632, 2048, 8), (2048, 5632, 8),
             (384, 256, 16), (37, 704, 3), (100, 32, 2), (256, 2048, 9), (130, 2048, 33),
-            (300, 6144, 130), (64, 256, 1), (4096, 6144, 2)]
+            (300, 6144, 130), (64, 256, 1), (4096, 6144, 2),
+            # the MFMA path with K stages not filled (3 and 65 blocks), ragged rows and tokens
+            (70, 96, 33), (129, 2080, 65), (200, 32, 100)]
 
 
 @pytest.mark.parametrize("n,k,m", MM_CASES)
@@ -168,7 +170,8 @@ def test_qmatmul_workload_seeded(gpu_lib):
             assert_same_fp32(host(y), ref)
 
 
-@pytest.mark.parametrize("ffn,k,m", [(5632, 2048, 1), (704, 256, 16), (96, 64, 5), (2048, 6144, 3)])
+@pytest.mark.parametrize("ffn,k,m", [(5632, 2048, 1), (704, 256, 16), (96, 64, 5), (2048, 6144, 3),
+                                     (100, 96, 70)])
 def test_gate_up_swiglu(gpu_lib, ffn, k, m):
     qk = gpu_lib
     say(f"qk_gate_up_swiglu ffn={ffn} k={k} m={m}")
@@ -316,6 +319,9 @@ ATT_CASES = [
     (2, 32, 4, 64, 8192, 2, "ring"),
     (3, 8, 2, 64, 100, 3, "ring"),
     (12, 16, 2, 64, 100, 12, "ring"),     # many tokens: the tiled pass
+    # head groups that do not divide the 64 query rows of a tiled-pass workgroup
+    (24, 12, 4, 64, 100, 2, "random"),    # G = 3: 21 tokens x 3 heads per workgroup
+    (25, 24, 4, 32, 90, 1, "prefill"),    # G = 6, head_dim 32
 ]
 
 
