@@ -251,9 +251,9 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     const int64_t unit0 = wg_unit0 + (int64_t)wave * upw;
 
     int c0 = 0, nc = a.m;
-    if (a.col_off) {
-        c0 = a.col_off[g];
-        nc = a.col_off[g + 1] - c0;
+    if (a.col_off) {   // uniform over the workgroup: keep them (and what they index) scalar
+        c0 = __builtin_amdgcn_readfirstlane(a.col_off[g]);
+        nc = __builtin_amdgcn_readfirstlane(a.col_off[g + 1]) - c0;
     }
     if (nc <= 0) return;   // uniform over the workgroup
 
@@ -286,40 +286,41 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const int col = cc + m < nc ? cc + m : nc - 1;  // clamp: extra columns are discarded
-            xr[m] = a.col_idx ? a.col_idx[c0 + col] : c0 + col;
+            xr[m] = a.col_idx ? __builtin_amdgcn_readfirstlane(a.col_idx[c0 + col]) : c0 + col;
         }
 
         uint4 w[RMAX][U];
-        float dw[RMAX][U];
-        float drs[RMAX];   // row scales (row-scaled formats)
-        // 32-bit offsets from the (uniform) matrix base: one matrix is below 4 GiB
+        uint16_t dwh[RMAX][U];   // fp16 block scales (Q4_0), converted where used
+        float drs[RMAX];         // row scales (row-scaled formats)
+        // 32-bit offsets from the (uniform) matrix base: one matrix is below
+        // 4 GiB.  The loads are unconditional, so that all of a step's loads
+        // issue before anything waits: a row past the matrix or a block past
+        // the row reads row 0 / block 0 instead, and those values are never
+        // used (the dot loop stops at the row's last block and rows past the
+        // matrix are not stored).
         auto load_w = [&](int64_t b0) {
 #pragma unroll
             for (int j = 0; j < RMAX; ++j) {
-                const uint32_t row = (uint32_t)prow(j);
+                const uint32_t row = rvalid(j) ? (uint32_t)prow(j) : 0u;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const uint32_t b = (uint32_t)b0 + u * WAVE + lane;
-                    dw[j][u] = 0.0f;
-                    if (rvalid(j) && b < (uint32_t)nb) {
-                        if (FMT == FMT_Q2_ROW) {
-                            const uint2 v = load_stream8(wq + (row * rowb + b * BB));
-                            w[j][u] = make_uint4(v.x, v.y, 0u, 0u);
-                        } else {
-                            w[j][u] = load_stream16(wq + (row * rowb + b * BB));
-                        }
-                        if (FMT == FMT_Q4_0)
-                            dw[j][u] = h2f(*reinterpret_cast<const uint16_t*>(
-                                reinterpret_cast<const char*>(wd) + (row * (uint32_t)nb + b) * 2u));
+                    uint32_t b = (uint32_t)b0 + u * WAVE + lane;
+                    b = b < (uint32_t)nb ? b : 0u;
+                    if (FMT == FMT_Q2_ROW) {
+                        const uint2 v = load_stream8(wq + (row * rowb + b * BB));
+                        w[j][u] = make_uint4(v.x, v.y, 0u, 0u);
                     } else {
-                        w[j][u] = make_uint4(0, 0, 0, 0);
+                        w[j][u] = load_stream16(wq + (row * rowb + b * BB));
                     }
+                    if (FMT == FMT_Q4_0)
+                        dwh[j][u] = *reinterpret_cast<const uint16_t*>(
+                            reinterpret_cast<const char*>(wd) + (row * (uint32_t)nb + b) * 2u);
                 }
             }
         };
         auto load_rs = [&]() {
 #pragma unroll
-            for (int j = 0; j < RMAX; ++j) drs[j] = (FMT != FMT_Q4_0 && rvalid(j)) ? wr[prow(j)] : 0.0f;
+            for (int j = 0; j < RMAX; ++j) drs[j] = FMT != FMT_Q4_0 ? wr[rvalid(j) ? prow(j) : 0] : 0.0f;
         };
 
         if (cc > 0) lds_barrier();   // the previous pass finished reading LDS
@@ -340,36 +341,37 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             // are loaded before the weights, the rest after
             constexpr int XREG = M == 1 ? 2 : (M == 2 ? 3 : 6);   // up to K = 6144 staged early
             const int64_t c16 = k / 16, tot = (int64_t)mc * c16, totd = (int64_t)mc * nb;
-            // activation row of pass column m (m < mc), looked up per use
+            // activation row of pass column m (m < mc), looked up per use (the
+            // lookups are unconditional, so they issue together)
             const int32_t* __restrict__ cidx = a.col_idx;
             auto col_row = [=](int m) -> int64_t {
                 const int col = c0 + cc + m;
                 return cidx ? (int64_t)cidx[col] : (int64_t)col;
             };
+            // (the loads are unconditional, so that none of them waits for
+            // another: a thread past the end reloads chunk 0 and stores nothing)
             uint4 xs[XREG];
-            float xds;
 #pragma unroll
             for (int p = 0; p < XREG; ++p) {
-                const int64_t i = threadIdx.x + (int64_t)p * 256;
-                xs[p] = make_uint4(0, 0, 0, 0);
-                if (i < tot) {
-                    const int64_t r = col_row((int)(i / c16));
-                    xs[p] = *reinterpret_cast<const uint4*>(a.xq + r * k + (i % c16) * 16);
-                }
+                int64_t i = threadIdx.x + (int64_t)p * 256;
+                i = i < tot ? i : 0;
+                const int64_t r = col_row((int)(i / c16));
+                xs[p] = *reinterpret_cast<const uint4*>(a.xq + r * k + (i % c16) * 16);
             }
-            xds = 0.0f;
-            if (threadIdx.x < totd) xds = h2f(a.xd[col_row((int)(threadIdx.x / nb)) * nb + threadIdx.x % nb]);
+            const int64_t id = (int64_t)threadIdx.x < totd ? (int64_t)threadIdx.x : 0;
+            const uint16_t xdh = a.xd[col_row((int)(id / nb)) * nb + id % nb];
             load_w(0);
             if (FMT != FMT_Q4_0) load_rs();
 #pragma unroll
-            for (int p = 0; p < XREG; ++p) {
-                const int64_t i = threadIdx.x + (int64_t)p * 256;
-                if (i < tot) *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) = xs[p];
+            for (int p = 0; p < XREG; ++p) {   // a thread past the end rewrites chunk 0 with itself
+                int64_t i = threadIdx.x + (int64_t)p * 256;
+                i = i < tot ? i : 0;
+                *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) = xs[p];
             }
             for (int64_t i = threadIdx.x + (int64_t)XREG * 256; i < tot; i += 256)
                 *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) =
                     *reinterpret_cast<const uint4*>(a.xq + col_row((int)(i / c16)) * k + (i % c16) * 16);
-            if (threadIdx.x < totd) lxd[threadIdx.x] = xds;
+            lxd[id] = h2f(xdh);
             for (int64_t i = threadIdx.x + 256; i < totd; i += 256)
                 lxd[i] = h2f(a.xd[col_row((int)(i / nb)) * nb + i % nb]);
         }
@@ -400,7 +402,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                             // dw * dx is exact in fp32 (two fp16 values); times
                             // the int32 block dot it is exact in fp64
                             const int sdot = dot_block(w[j][u], x0, x1, s0);
-                            acc[j][m] = fma((double)(dw[j][u] * dx), (double)sdot, acc[j][m]);
+                            acc[j][m] = fma((double)(h2f(dwh[j][u]) * dx), (double)sdot, acc[j][m]);
                         } else {
                             const int sdot = FMT == FMT_Q2_ROW ? dot_block2(w[j][u], x0, x1, s0)
                                                                : dot_block(w[j][u], x0, x1, s0);

@@ -24,7 +24,8 @@ namespace qk {
 namespace {
 
 constexpr int RT = 4;        // tokens per router workgroup
-constexpr int RSLICE = 768;  // hidden elements per router slice
+constexpr int RSLICE = 384;  // hidden elements per router slice
+constexpr int RUNROLL = 16;  // router weight loads issued together
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -87,10 +88,21 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
     double acc[RT];
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0;
-    for (int64_t hh = 0; hh < hn; ++hh) {
-        const double w = wr[(h0 + hh) * E + e];
+    const float* __restrict__ wcol = wr + h0 * E + e;
+    int h1 = 0;
+    for (; h1 + RUNROLL <= (int)hn; h1 += RUNROLL) {
+        float w[RUNROLL];   // all loads of the group first, so their latencies overlap
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][hh], w, acc[tt]);
+        for (int q = 0; q < RUNROLL; ++q) w[q] = wcol[(int64_t)(h1 + q) * E];
+#pragma unroll
+        for (int q = 0; q < RUNROLL; ++q)
+#pragma unroll
+            for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][h1 + q], (double)w[q], acc[tt]);
+    }
+    for (; h1 < (int)hn; ++h1) {   // ragged end of the last slice
+        const double w = wcol[(int64_t)h1 * E];
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][h1], w, acc[tt]);
     }
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt)
