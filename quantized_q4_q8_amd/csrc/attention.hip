@@ -66,16 +66,22 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
     const int rows = (int)min((int64_t)ACH, pe + 1 - r0);
     const double rscale = sqrt((double)HD);
 
-    for (int i = tid; i < G * HD; i += 512)
-        qs[i / HD][i % HD] = (double)q[t * q_ts + (g * G) * HD + i];
+    // One q value and one 8-value piece of a K and a V row per thread
+    // (G * HD <= 512 and ACH * HD / 8 <= 512).  The three loads are
+    // unconditional, with indexes clamped into the chunk, so that they are
+    // all in flight before anything waits; rows past the last attended one
+    // are staged but never read.
+    static_assert(ACH * HD / 8 <= 512, "one K/V piece per thread");
+    const int iq = tid < G * HD ? tid : 0;
+    const float qv = q[t * q_ts + (g * G) * HD + iq];
     const int64_t cbase = (((int64_t)seq[t] * nkv + g) * cap + r0) * HD;
-    for (int i = tid; i < ACH * HD / 8; i += 512) {
-        const int r = (i * 8) / HD, d = (i * 8) % HD;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (r < rows) {
-            kv = *reinterpret_cast<const uint4*>(kc + cbase + (int64_t)r * HD + d);
-            vv = *reinterpret_cast<const uint4*>(vc + cbase + (int64_t)r * HD + d);
-        }
+    const int i = tid < ACH * HD / 8 ? tid : 0;
+    const int r = (i * 8) / HD, d = (i * 8) % HD;
+    const int64_t roff = (int64_t)(r < rows ? r : 0) * HD + d;
+    const uint4 kv = *reinterpret_cast<const uint4*>(kc + cbase + roff);
+    const uint4 vv = *reinterpret_cast<const uint4*>(vc + cbase + roff);
+    if (tid < G * HD) qs[tid / HD][tid % HD] = (double)qv;
+    if (tid < ACH * HD / 8) {
         const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
         float4 k0, k1, v0, v1;
         k0.x = h2f((uint16_t)(kw[0] & 0xFFFF)); k0.y = h2f((uint16_t)(kw[0] >> 16));

@@ -92,9 +92,11 @@ __device__ __forceinline__ int dot_block2(const uint4 w, const uint4 x0, const u
 
 // Workgroup-wide RMSNorm / Q8_0 of one activation row into LDS.  Each lane
 // takes 8 consecutive values per 2048-value chunk (four lanes per Q8_0 block),
-// with the same arithmetic as the standalone quantizer.  The row's global
-// loads are issued by `load_row` before the caller issues its weight loads,
-// so that waiting on them leaves the weight loads in flight.
+// with the same arithmetic as the standalone quantizer.  `load_row` loads
+// under a bounds test, so the row has arrived before the caller's weight
+// loads go out; the norm and the LDS staging then overlap the weight loads.
+// (Issuing the weight loads before the row has arrived measured slower: the
+// row, read by every workgroup, then queues behind the weight misses.)
 constexpr int PRO_CHUNKS = 3;  // rows up to 3 * 2048 values
 
 template <int KC>
@@ -327,7 +329,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         if (PRO != PRO_NONE) {
             RowRegs<KC> Rg;
             load_row<PRO, KC>(Rg, a.xf + (int64_t)xr[0] * k, a.gamma, k);
-            load_w(0);                    // weight loads go out behind the row loads
+            load_w(0);                    // issued once the row has arrived
             stage_row<PRO, KC>(Rg, k, a.eps, red, lxq, lxd);
 #pragma unroll
             for (int m = 1; m < M; ++m) {
