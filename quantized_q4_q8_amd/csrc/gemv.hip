@@ -586,19 +586,22 @@ size_t stage_bytes(int M, int64_t k) {
     return (((size_t)M * k + (size_t)M * (k / QBLK) * 4) + 7) & ~(size_t)7;
 }
 
-// Physical rows per wave.  Kernels that stage their activations with a
-// fused RMSNorm prologue run two units per wave (fewer workgroups repeat the
-// prologue); the others one unit per wave until the launch has more than
-// 8192 units, then two, then four (two at most for 4 or 8 columns per pass,
-// or for Q4_0 rows longer than 64 blocks, whose block scales take registers:
+// Physical rows per wave, at most four (two for 4 or 8 columns per pass, or
+// for Q4_0 rows longer than 64 blocks, whose block scales take registers:
 // four rows of them drop the grouped SwiGLU GEMV of the MoE layer to two
 // waves per SIMD, while the row-scaled formats keep three and gain).
-// Small per-wave work and many waves keep the most loads in flight per CU.
+// Kernels that stage their activations with a fused prologue (RMSNorm or
+// Q8_0 of an fp32 row) take the most rows allowed, so that fewer workgroups
+// repeat the prologue: on the 22-layer decode step this measured 5% faster
+// than one unit per wave for the QKV and down projections, and eight rows
+// per wave measured slower again.  The others run one unit per wave until
+// the launch has more than 8192 units, then two, then four: small per-wave
+// work and many waves keep the most loads in flight per CU.
 int pick_rows(int epi, int pro, int M, int64_t k, int64_t units, int fmt = FMT_Q4_0) {
     const int P = rows_per_unit(epi);
     const int cap = (M <= 2 && (k / QBLK <= WAVE || fmt != FMT_Q4_0)) ? 4 : 2;
     int upw = units > 2 * 8192 ? 4 : (units > 8192 ? 2 : 1);
-    if (pro == PRO_RMSNORM && epi == EPI_SWIGLU && units >= 2048) upw = std::max(upw, 2);
+    if (pro != PRO_NONE) upw = 4;
     while (upw * P > cap) upw /= 2;
     return std::max(1, upw) * P;
 }
