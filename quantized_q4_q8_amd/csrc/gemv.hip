@@ -19,6 +19,8 @@
 // (row_sums) and the epilogue runs in the lanes that hold them.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace qk {
 
 namespace {
@@ -235,6 +237,16 @@ __host__ __device__ constexpr int rows_per_unit(int epi) {
 // FMT: Q4_0 (fp16 scale per block), or row-scaled int4 / int2 (fp32 scale
 // per row): their block sums are dx * isum, and the row's scale multiplies
 // the row's total in the epilogue, once.
+// Column of 16-byte chunk (or block) i of a pass whose columns hold `per`
+// each (i < M * per): M - 1 compares instead of a division.
+template <int M>
+__device__ __forceinline__ uint32_t col_of(uint32_t i, uint32_t per) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 1; q < M; ++q) m += i >= (uint32_t)q * per ? 1u : 0u;
+    return m;
+}
+
 template <int FMT, int M, int R, int U, int EPI, int PRO, int KC, bool KLOOP>
 __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -282,8 +294,18 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     float* lxd = reinterpret_cast<float*>(smem + (size_t)M * k);
     double* ltail = reinterpret_cast<double*>(smem + (((size_t)M * k + (size_t)M * nb * 4 + 7) & ~(size_t)7));
 
-    for (int cc = 0; cc < nc; cc += M) {
+    // Weight registers.  When the row share fits one step (!KLOOP) they are
+    // loaded by the first column pass and kept for the others, so a group
+    // with more columns than one pass takes reads its weights once (the
+    // loads are non-temporal: a second pass would fetch them again).  The
+    // first pass is a separate instantiation of the pass body, so that its
+    // loads stay in one basic block and issue in the order written.
+    uint4 w[RMAX][U];
+    uint16_t dwh[RMAX][U];   // fp16 block scales (Q4_0), converted where used
+    auto pass = [&](const int cc, auto first) __attribute__((always_inline)) {
+        constexpr bool load_now = decltype(first)::value || KLOOP;
         const int mc = nc - cc < M ? nc - cc : M;
+        float drs[RMAX];     // row scales (row-scaled formats), loaded by every pass
         int xr[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -291,9 +313,6 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             xr[m] = a.col_idx ? __builtin_amdgcn_readfirstlane(a.col_idx[c0 + col]) : c0 + col;
         }
 
-        uint4 w[RMAX][U];
-        uint16_t dwh[RMAX][U];   // fp16 block scales (Q4_0), converted where used
-        float drs[RMAX];         // row scales (row-scaled formats)
         // 32-bit offsets from the (uniform) matrix base: one matrix is below
         // 4 GiB.  The loads are unconditional, so that all of a step's loads
         // issue before anything waits: a row past the matrix or a block past
@@ -329,7 +348,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         if (PRO != PRO_NONE) {
             RowRegs<KC> Rg;
             load_row<PRO, KC>(Rg, a.xf + (int64_t)xr[0] * k, a.gamma, k);
-            load_w(0);                    // issued once the row has arrived
+            if constexpr (load_now) load_w(0);   // issued once the row has arrived
             stage_row<PRO, KC>(Rg, k, a.eps, red, lxq, lxd);
 #pragma unroll
             for (int m = 1; m < M; ++m) {
@@ -342,40 +361,61 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             // copy the Q8_0 columns into LDS: the first XREG chunks per thread
             // are loaded before the weights, the rest after
             constexpr int XREG = M == 1 ? 2 : (M == 2 ? 3 : 6);   // up to K = 6144 staged early
-            const int64_t c16 = k / 16, tot = (int64_t)mc * c16, totd = (int64_t)mc * nb;
+            // 16-byte chunks per column, chunk counts of the pass (32-bit:
+            // K and the column count are small)
+            const uint32_t c16 = (uint32_t)k / 16u, unb = (uint32_t)nb;
+            const uint32_t tot = (uint32_t)mc * c16, totd = (uint32_t)mc * unb;
             // activation row of pass column m (m < mc), looked up per use (the
             // lookups are unconditional, so they issue together)
             const int32_t* __restrict__ cidx = a.col_idx;
-            auto col_row = [=](int m) -> int64_t {
-                const int col = c0 + cc + m;
+            auto col_row = [=](uint32_t m) -> int64_t {
+                const int col = c0 + cc + (int)m;
                 return cidx ? (int64_t)cidx[col] : (int64_t)col;
             };
+            const uint32_t id = threadIdx.x < totd ? threadIdx.x : 0u;
+            const uint32_t md = col_of<M>(id, unb);
+            uint16_t xdh;
+            if constexpr (load_now && !KLOOP) {
             // (the loads are unconditional, so that none of them waits for
             // another: a thread past the end reloads chunk 0 and stores nothing)
             uint4 xs[XREG];
 #pragma unroll
             for (int p = 0; p < XREG; ++p) {
-                int64_t i = threadIdx.x + (int64_t)p * 256;
-                i = i < tot ? i : 0;
-                const int64_t r = col_row((int)(i / c16));
-                xs[p] = *reinterpret_cast<const uint4*>(a.xq + r * k + (i % c16) * 16);
+                uint32_t i = threadIdx.x + (uint32_t)p * 256u;
+                i = i < tot ? i : 0u;
+                const uint32_t m = col_of<M>(i, c16);
+                xs[p] = *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
             }
-            const int64_t id = (int64_t)threadIdx.x < totd ? (int64_t)threadIdx.x : 0;
-            const uint16_t xdh = a.xd[col_row((int)(id / nb)) * nb + id % nb];
+            xdh = a.xd[col_row(md) * nb + (id - md * unb)];
             load_w(0);
             if (FMT != FMT_Q4_0) load_rs();
 #pragma unroll
             for (int p = 0; p < XREG; ++p) {   // a thread past the end rewrites chunk 0 with itself
-                int64_t i = threadIdx.x + (int64_t)p * 256;
-                i = i < tot ? i : 0;
-                *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) = xs[p];
+                uint32_t i = threadIdx.x + (uint32_t)p * 256u;
+                i = i < tot ? i : 0u;
+                const uint32_t m = col_of<M>(i, c16);
+                *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) = xs[p];
             }
-            for (int64_t i = threadIdx.x + (int64_t)XREG * 256; i < tot; i += 256)
-                *reinterpret_cast<uint4*>(lxq + (i / c16) * k + (i % c16) * 16) =
-                    *reinterpret_cast<const uint4*>(a.xq + col_row((int)(i / c16)) * k + (i % c16) * 16);
+            for (uint32_t i = threadIdx.x + (uint32_t)XREG * 256u; i < tot; i += 256u) {
+                const uint32_t m = col_of<M>(i, c16);
+                *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) =
+                    *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
+            }
+            } else {   // later passes (weights in registers already), or rows of several steps
+            xdh = a.xd[col_row(md) * nb + (id - md * unb)];
+            if constexpr (load_now) load_w(0);
+            if (FMT != FMT_Q4_0) load_rs();
+            for (uint32_t i = threadIdx.x; i < tot; i += 256u) {
+                const uint32_t m = col_of<M>(i, c16);
+                *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) =
+                    *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
+            }
+            }
             lxd[id] = h2f(xdh);
-            for (int64_t i = threadIdx.x + 256; i < totd; i += 256)
-                lxd[i] = h2f(a.xd[col_row((int)(i / nb)) * nb + i % nb]);
+            for (uint32_t i = threadIdx.x + 256u; i < totd; i += 256u) {
+                const uint32_t m = col_of<M>(i, unb);
+                lxd[i] = h2f(a.xd[col_row(m) * nb + (i - m * unb)]);
+            }
         }
         lds_barrier();
 
@@ -527,6 +567,14 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                 a.part_idx[(int64_t)(cc + mm) * gridDim.x + blockIdx.x] = besti;
             }
         }
+    };
+    if constexpr (KLOOP || PRO != PRO_NONE) {
+        // (fused-prologue kernels keep loading per pass: their own row
+        // staging must come first, and their passes are rare)
+        for (int cc = 0; cc < nc; cc += M) pass(cc, std::true_type{});
+    } else {
+        pass(0, std::true_type{});
+        for (int cc = M; cc < nc; cc += M) pass(cc, std::false_type{});
     }
 }
 
