@@ -24,8 +24,7 @@ namespace qk {
 namespace {
 
 constexpr int RT = 4;        // tokens per router workgroup
-constexpr int RSLICE = 384;  // hidden elements per router slice
-constexpr int RUNROLL = 16;  // router weight loads issued together
+constexpr int RSLICE = 128;  // hidden elements per router slice: all its loads issue together
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -89,127 +88,149 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0;
     const float* __restrict__ wcol = wr + h0 * E + e;
-    int h1 = 0;
-    for (; h1 + RUNROLL <= (int)hn; h1 += RUNROLL) {
-        float w[RUNROLL];   // all loads of the group first, so their latencies overlap
+    if (hn == RSLICE) {
+        // every load of the slice first (unconditional), so one memory
+        // latency covers the slice
+        float w[RSLICE];
 #pragma unroll
-        for (int q = 0; q < RUNROLL; ++q) w[q] = wcol[(int64_t)(h1 + q) * E];
+        for (int q = 0; q < RSLICE; ++q) w[q] = wcol[(int64_t)q * E];
 #pragma unroll
-        for (int q = 0; q < RUNROLL; ++q)
+        for (int q = 0; q < RSLICE; ++q)
 #pragma unroll
-            for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][h1 + q], (double)w[q], acc[tt]);
-    }
-    for (; h1 < (int)hn; ++h1) {   // ragged end of the last slice
-        const double w = wcol[(int64_t)h1 * E];
+            for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][q], (double)w[q], acc[tt]);
+    } else {   // ragged last slice
+        for (int h1 = 0; h1 < (int)hn; ++h1) {
+            const double w = wcol[(int64_t)h1 * E];
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][h1], w, acc[tt]);
+            for (int tt = 0; tt < RT; ++tt) acc[tt] = fma((double)xs[tt][h1], w, acc[tt]);
+        }
     }
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt)
         if (t0 + tt < T) rpart[(s * T + t0 + tt) * E + e] = acc[tt];
 }
 
-// One workgroup (256 threads) per token: r[e] from the slices in order, then
-// top-k by repeated (value, lowest index) maxima over the experts not yet
-// taken (NaN never wins), then sigmoid weights normalized over the choice.
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ rpart, int64_t slices,
-                                              int64_t T, int64_t E, int32_t k,
-                                              int32_t* __restrict__ sel_idx,
-                                              float* __restrict__ sel_w) {
-    __shared__ float rv[1024];
-    __shared__ unsigned char taken[1024];
-    __shared__ float wv[4];
-    __shared__ int wi[4];
-    __shared__ int chosen_e[32];
+// One workgroup (1024 threads) per token: r[e] from the slices in order,
+// then the top k in one pass: thread e counts the experts that come before it
+// in the order (value descending, lower index first among equal values, NaN
+// after every number and among NaNs by index), which is the order of
+// repeated maxima over the experts not yet taken, and writes itself to
+// slot `rank` when rank < k.  Sigmoid weights are normalized over the choice
+// (the sum in rank order).
+__global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ rpart, int64_t slices,
+                                               int64_t T, int64_t E, int32_t k,
+                                               int32_t* __restrict__ sel_idx,
+                                               float* __restrict__ sel_w) {
+    __shared__ __align__(16) float rv[1024];
+    __shared__ int chosen[32];
+    __shared__ double sg[32];
     const int64_t t = blockIdx.x;
-    for (int64_t e = threadIdx.x; e < E; e += 256) {
+    const int tid = threadIdx.x;
+    if (tid < E) {   // slice partials in slice order, eight loads in flight at a time
         double r = 0.0;
-        for (int64_t s = 0; s < slices; ++s) r += rpart[(s * T + t) * E + e];
-        rv[e] = (float)r;
-        taken[e] = 0;
+        int64_t s = 0;
+        for (; s + 8 <= slices; s += 8) {
+            double v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = rpart[((s + i) * T + t) * E + tid];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r += v[i];
+        }
+        for (; s < slices; ++s) r += rpart[(s * T + t) * E + tid];
+        rv[tid] = (float)r;
     }
     __syncthreads();
-    for (int kk = 0; kk < k; ++kk) {
-        float bv = -INFINITY;
-        int bi = INT32_MAX;
-        for (int64_t e = threadIdx.x; e < E; e += 256) {
-            if (taken[e]) continue;
-            const float v = rv[e];
-            if (v > bv || (v == bv && (int)e < bi)) { bv = v; bi = (int)e; }
-        }
+    if (tid < E) {
+        const float v = rv[tid];
+        const bool vnan = v != v;
+        int rank = 0;
+        for (int j4 = 0; j4 < (int)E; j4 += 4) {   // rv is read four entries at a time
+            const float4 q = *reinterpret_cast<const float4*>(&rv[j4]);
+            const float qv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, WAVE);
-            const int oi = __shfl_xor(bi, o, WAVE);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            for (int i = 0; i < 4; ++i) {
+                const int j = j4 + i;
+                const float u = qv[i];
+                const bool unan = u != u;
+                const bool before = vnan ? (!unan || j < tid)
+                                         : (!unan && (u > v || (u == v && j < tid)));
+                rank += (j < (int)E && before) ? 1 : 0;
+            }
         }
-        if ((threadIdx.x & 63) == 0) { wv[threadIdx.x >> 6] = bv; wi[threadIdx.x >> 6] = bi; }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int w = 1; w < 4; ++w)
-                if (wv[w] > bv || (wv[w] == bv && wi[w] < bi)) { bv = wv[w]; bi = wi[w]; }
-            if (bi == INT32_MAX)  // only NaN left: the lowest index not taken
-                for (int e = 0; e < E; ++e)
-                    if (!taken[e]) { bi = e; break; }
-            chosen_e[kk] = bi;
-            taken[bi] = 1;
-        }
-        __syncthreads();
+        if (rank < k) chosen[rank] = tid;
     }
-    if (threadIdx.x == 0) {
+    __syncthreads();
+    if (tid < k) sg[tid] = 1.0 / (1.0 + exp(-(double)rv[chosen[tid]]));
+    __syncthreads();
+    if (tid == 0) {
         double ssum = 0.0;
-        for (int kk = 0; kk < k; ++kk) ssum += 1.0 / (1.0 + exp(-(double)rv[chosen_e[kk]]));
+        for (int kk = 0; kk < k; ++kk) ssum += sg[kk];
         for (int kk = 0; kk < k; ++kk) {
-            const double sv = 1.0 / (1.0 + exp(-(double)rv[chosen_e[kk]]));
-            sel_idx[t * k + kk] = chosen_e[kk];
-            sel_w[t * k + kk] = (float)(sv / ssum);
+            sel_idx[t * k + kk] = chosen[kk];
+            sel_w[t * k + kk] = (float)(sg[kk] / ssum);
         }
     }
 }
 
 // Stable counting sort of the P = T * k pairs by expert (one workgroup of
-// 1024 threads).  Pairs are taken in chunks of 1024 in pair order; a pair's
-// column is off[e] + (pairs of e in earlier chunks) + (pairs of e earlier in
-// its chunk), so columns of an expert follow (token, rank) order.
+// 1024 threads).  Counts by LDS atomics; the expert offsets by a workgroup
+// scan (thread e owns expert e).  Pairs are then taken in chunks of 1024 in
+// pair order; a pair's column is off[e] + (pairs of e in earlier chunks) +
+// (pairs of e earlier in its chunk), so columns of an expert follow
+// (token, rank) order.
 __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ sel_idx, int64_t P,
                                                 int32_t k, int64_t E, int32_t* __restrict__ off,
                                                 int32_t* __restrict__ col_tok,
                                                 int32_t* __restrict__ slot) {
     __shared__ int cnt[1024];
     __shared__ int base[1024];
-    __shared__ int chunk_e[1024];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    __shared__ __align__(16) int chunk_e[1024];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < E) cnt[tid] = 0;
     __syncthreads();
     for (int64_t p = tid; p < P; p += 1024) atomicAdd(&cnt[sel_idx[p]], 1);
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = run;
-            base[e] = run;
-            run += cnt[e];
-        }
-        off[E] = run;
+    // exclusive scan of the counts: inclusive within each wave, then the
+    // totals of the waves before
+    const int c = tid < E ? cnt[tid] : 0;
+    int inc = c;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(inc, d, WAVE);
+        if (lane >= d) inc += o;
+    }
+    if (lane == WAVE - 1) wsum[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + inc - c;
+    if (tid < E) {
+        off[tid] = excl;
+        base[tid] = excl;
+        if (tid == E - 1) off[E] = excl + c;
     }
     __syncthreads();
     for (int64_t c0 = 0; c0 < P; c0 += 1024) {
         const int64_t p = c0 + tid;
+        const int n = (int)min((int64_t)1024, P - c0);
         const int e = p < P ? sel_idx[p] : -1;
         chunk_e[tid] = e;
         __syncthreads();
         if (p < P) {
             int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += chunk_e[q] == e;
+            int q = 0;
+            for (; q + 4 <= tid; q += 4) {   // four entries per read
+                const int4 v = *reinterpret_cast<const int4*>(&chunk_e[q]);
+                rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+            }
+            for (; q < tid; ++q) rank += chunk_e[q] == e;
             const int col = base[e] + rank;
             col_tok[col] = (int32_t)(p / k);
             slot[p] = col;
         }
-        __syncthreads();
-        if (tid == 0) {
-            const int64_t n = min((int64_t)1024, P - c0);
-            for (int q = 0; q < n; ++q) base[chunk_e[q]] += 1;
-        }
+        __syncthreads();   // every pair of the chunk has read base
+        if (tid < n) atomicAdd(&base[e], 1);
         __syncthreads();
     }
 }
@@ -274,7 +295,7 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     hipLaunchKernelGGL(k_router, dim3((unsigned)((E + 255) / 256), (unsigned)((T + RT - 1) / RT),
                                       (unsigned)slices),
                        dim3(256), 0, s, x, T, H, w_router, E, w.rpart);
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(256), 0, s, w.rpart, slices, T, E, top_k,
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(1024), 0, s, w.rpart, slices, T, E, top_k,
                        sel_idx, sel_w);
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, sel_idx, P, top_k, E, w.off, w.col_tok,
                        w.slot);

@@ -228,6 +228,31 @@ def test_moe_rowq_matches_oracle(gpu_lib, bits, T, H, E, F, k):
     assert all(len(set(r)) == k for r in sel_g)
 
 
+@pytest.mark.parametrize("E,k", [(256, 8), (1001, 32), (37, 5)])
+def test_moe_router_exact_ties(gpu_lib, E, k):
+    """Router columns repeat seven distinct columns, so every token's logits
+    tie exactly in groups; the choice must be the oracle's (largest logit,
+    lower expert index among equal logits), for the expert count of the MoE
+    workload, the largest supported count with a ragged tail, and a small one."""
+    qk = gpu_lib
+    T, H, F = 20, 64, 32
+    say(f"moe router exact ties E={E} k={k}")
+    seed = 70 + E
+    x = synth.normal(seed, W.TID_X, (T, H))
+    base = synth.normal(seed, W.TID_ROUTER, (H, 7), 0.02)
+    wr = np.ascontiguousarray(base[:, np.arange(E) % 7])
+    gu, dn = experts_f32(seed, E, H, F)
+    guq = np.stack([oracle.quantize_q4_0(a)[0] for a in gu])
+    gud = np.stack([oracle.quantize_q4_0(a)[1] for a in gu])
+    dnq = np.stack([oracle.quantize_q4_0(a)[0] for a in dn])
+    dnd = np.stack([oracle.quantize_q4_0(a)[1] for a in dn])
+    out, sel, w = oracle.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd)
+    y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
+    assert np.array_equal(host(sg), sel)
+    assert np.allclose(host(wg), w, rtol=1e-6, atol=1e-8)
+    assert rel_err(host(y), out) < LAYER_TOL
+
+
 def test_moe_zero_router_ties(gpu_lib):
     qk = gpu_lib
     T, H, E, F, k = 4, 64, 12, 32, 5
