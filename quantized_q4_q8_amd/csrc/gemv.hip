@@ -635,9 +635,9 @@ size_t stage_bytes(int M, int64_t k) {
 }
 
 // Physical rows per wave, at most four (two for 4 or 8 columns per pass, or
-// for Q4_0 rows longer than 64 blocks, whose block scales take registers:
-// four rows of them drop the grouped SwiGLU GEMV of the MoE layer to two
-// waves per SIMD, while the row-scaled formats keep three and gain).
+// for Q4_0 rows longer than 64 blocks behind a fused prologue: four rows
+// measured slower for the decode down projection, while the grouped SwiGLU
+// GEMV of the MoE layer, without a prologue, gained 5% from them).
 // Kernels that stage their activations with a fused prologue (RMSNorm or
 // Q8_0 of an fp32 row) take the most rows allowed, so that fewer workgroups
 // repeat the prologue: on the 22-layer decode step this measured 5% faster
@@ -647,7 +647,7 @@ size_t stage_bytes(int M, int64_t k) {
 // work and many waves keep the most loads in flight per CU.
 int pick_rows(int epi, int pro, int M, int64_t k, int64_t units, int fmt = FMT_Q4_0) {
     const int P = rows_per_unit(epi);
-    const int cap = (M <= 2 && (k / QBLK <= WAVE || fmt != FMT_Q4_0)) ? 4 : 2;
+    const int cap = (M <= 2 && (k / QBLK <= WAVE || fmt != FMT_Q4_0 || pro == PRO_NONE)) ? 4 : 2;
     int upw = units > 2 * 8192 ? 4 : (units > 8192 ? 2 : 1);
     if (pro != PRO_NONE) upw = 4;
     while (upw * P > cap) upw /= 2;

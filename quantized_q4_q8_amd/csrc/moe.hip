@@ -110,53 +110,82 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
         if (t0 + tt < T) rpart[(s * T + t0 + tt) * E + e] = acc[tt];
 }
 
-// One workgroup (1024 threads) per token: r[e] from the slices in order,
-// then the top k in one pass: thread e counts the experts that come before it
-// in the order (value descending, lower index first among equal values, NaN
-// after every number and among NaNs by index), which is the order of
-// repeated maxima over the experts not yet taken, and writes itself to
-// slot `rank` when rank < k.  Sigmoid weights are normalized over the choice
-// (the sum in rank order).
+// One workgroup (1024 threads) per token: r[e] from the slice partials,
+// then the top k in one pass: expert e's rank is the number of experts that
+// come before it in the order (value descending, lower index first among
+// equal values, NaN after every number and among NaNs by index), which is
+// the order of repeated maxima over the experts not yet taken; the expert
+// with rank < k goes to slot `rank`.  Sigmoid weights are normalized over
+// the choice (the sum in rank order).
+//
+// Thread (g, e) of G groups sums slices g, g + G, ... for expert e, and then
+// counts the experts j of its quarter (g-th G-th) of the index range that
+// come before e; both are added over the groups in group order.  Values are
+// compared as order-preserving integer keys: NaN is 0, below every number,
+// and -0 and +0 share a key.
+__device__ __forceinline__ uint32_t route_key(float v) {
+    if (v != v) return 0u;
+    const uint32_t b = __float_as_uint(v + 0.0f);   // -0 -> +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ rpart, int64_t slices,
                                                int64_t T, int64_t E, int32_t k,
                                                int32_t* __restrict__ sel_idx,
                                                float* __restrict__ sel_w) {
-    __shared__ __align__(16) float rv[1024];
+    __shared__ float rv[1024];
+    __shared__ __align__(16) uint32_t key[1024];
+    __shared__ double part[1024];
+    __shared__ int prank[1024];
     __shared__ int chosen[32];
     __shared__ double sg[32];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < E) {   // slice partials in slice order, eight loads in flight at a time
+    const int ep = (int)((E + WAVE - 1) / WAVE) * WAVE;   // experts rounded to waves
+    const int G = 1024 / ep;
+    const int g = tid / ep, e = tid % ep;
+    const bool act = g < G && e < E;
+    if (act) {   // eight loads in flight at a time
         double r = 0.0;
-        int64_t s = 0;
-        for (; s + 8 <= slices; s += 8) {
+        int64_t s = g;
+        for (; s + 7 * G < slices; s += 8 * G) {
             double v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = rpart[((s + i) * T + t) * E + tid];
+            for (int i = 0; i < 8; ++i) v[i] = rpart[((s + i * G) * T + t) * E + e];
 #pragma unroll
             for (int i = 0; i < 8; ++i) r += v[i];
         }
-        for (; s < slices; ++s) r += rpart[(s * T + t) * E + tid];
-        rv[tid] = (float)r;
+        for (; s < slices; s += G) r += rpart[(s * T + t) * E + e];
+        part[g * ep + e] = r;
     }
     __syncthreads();
     if (tid < E) {
-        const float v = rv[tid];
-        const bool vnan = v != v;
+        double r = 0.0;
+        for (int q = 0; q < G; ++q) r += part[q * ep + tid];
+        rv[tid] = (float)r;
+        key[tid] = route_key((float)r);
+    }
+    __syncthreads();
+    if (act) {
+        const uint32_t ke = key[e];
+        const int per = ((ep + G - 1) / G + 3) & ~3;   // this group's index range, a multiple of 4
+        const int j0 = g * per, j1 = min((int)E, j0 + per);
         int rank = 0;
-        for (int j4 = 0; j4 < (int)E; j4 += 4) {   // rv is read four entries at a time
-            const float4 q = *reinterpret_cast<const float4*>(&rv[j4]);
-            const float qv[4] = {q.x, q.y, q.z, q.w};
+        for (int j4 = j0; j4 < j1; j4 += 4) {   // four keys per read (j1 <= E <= 1024)
+            const uint4 q = *reinterpret_cast<const uint4*>(&key[j4]);
+            const uint32_t kq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = j4 + i;
-                const float u = qv[i];
-                const bool unan = u != u;
-                const bool before = vnan ? (!unan || j < tid)
-                                         : (!unan && (u > v || (u == v && j < tid)));
-                rank += (j < (int)E && before) ? 1 : 0;
+                rank += (j < j1 && (kq[i] > ke || (kq[i] == ke && j < e))) ? 1 : 0;
             }
         }
+        prank[g * ep + e] = rank;
+    }
+    __syncthreads();
+    if (tid < E) {
+        int rank = 0;
+        for (int q = 0; q < G; ++q) rank += prank[q * ep + tid];
         if (rank < k) chosen[rank] = tid;
     }
     __syncthreads();
