@@ -33,6 +33,29 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def read_ceiling(dev) -> float:
+    """Achievable HBM read rate (GB/s): qk_read_probe streaming a 1 GiB
+    buffer (four times the memory-side cache) with the GEMV's 128-bit
+    non-temporal loads, 10 timed passes after 2 untimed."""
+    import torch
+    import quantized_q4_q8_amd as qk
+    buf = torch.zeros(2**30 // 4, dtype=torch.int32, device=dev)
+    words = torch.empty(2048, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        qk.qk_read_probe(buf, out=words)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        qk.qk_read_probe(buf, out=words)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2**30 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf, words
+    log(f"read probe: {gbs:.0f} GB/s achievable (1 GiB, 128-bit non-temporal loads)")
+    return gbs
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +263,7 @@ def run_decode(args, long_context: bool = False):
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
+    read_gbs = read_ceiling(dev)
 
     step_bytes = decode_bytes_per_token(spec)
     c0, c1 = spec["context"], spec["context"] + steps_per_run - 1
@@ -272,7 +296,8 @@ def run_decode(args, long_context: bool = False):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": int(kbytes),
                      "avg_us": round(avg_us, 3), "launches_timed": args.kernel_rounds * L,
-                     "source_hash": src},
+                     "source_hash": src, "achievable_GBps": round(read_gbs, 1),
+                     "frac_of_achievable": round(achieved / read_gbs, 4)},
         "step_roofline": {"bytes_per_token": int(step_bytes),
                           "achieved_GBps": round(step_bytes * tok_s / 1e9, 1),
                           "frac": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -410,6 +435,9 @@ def run_matmul(args):
                        "achieved": head["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(head["cold_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
                        "bytes_per_launch": head["bytes_per_launch"], "avg_us": head["cold_us"]}
+    read_gbs = read_ceiling(dev)
+    out["roofline"]["achievable_GBps"] = round(read_gbs, 1)
+    out["roofline"]["frac_of_achievable"] = round(head["cold_GBps"] / read_gbs, 4)
     out["shapes"] = rows
     if not args.no_cpu_baseline:
         import oracle
@@ -584,6 +612,9 @@ def run_moe(args):
                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
                        "avg_us": round(us, 2)}
+    read_gbs = read_ceiling(dev)
+    out["roofline"]["achievable_GBps"] = round(read_gbs, 1)
+    out["roofline"]["frac_of_achievable"] = round(gbs / read_gbs, 4)
     if not args.no_cpu_baseline:
         import oracle
         xs = normal(seed, W.TID_X, (T, H))[:1]

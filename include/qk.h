@@ -341,6 +341,19 @@ int qk_moe_route_and_apply_rowq(int32_t bits, const float* x, int64_t tokens, in
                                 int32_t* sel_idx, float* sel_w, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Measurement                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* Achievable read rate, for the rooflines of the streaming kernels (not an
+ * operation of the method): reads `bytes` (a multiple of 16) of device
+ * memory at `buf` (16-byte aligned) with 128-bit non-temporal loads in a
+ * grid-stride loop over `blocks` workgroups of 256 threads (1..65536), and
+ * writes the XOR of the words each workgroup read to out[blocks] (device,
+ * uint32).  The caller times it.  QK_EINVAL / QK_ESHAPE / QK_EALIGN for bad
+ * arguments; bytes == 0 still launches and writes zeros. */
+int qk_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

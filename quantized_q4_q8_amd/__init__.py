@@ -58,6 +58,7 @@ _SIGS = {
     "swiglu": ([_P, _P, _I64, _P, _P], ctypes.c_int),
     "qk_kv_append": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "qk_embed_lookup": ([_P, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "qk_read_probe": ([_P, _I64, _P, ctypes.c_int32, _P], ctypes.c_int),
     "qk_sample": ([_P, _I64, _I64, ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, _P, _P],
                   ctypes.c_int),
     "qk_argmax": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
@@ -300,6 +301,18 @@ def qk_sample(logits, top_k: int, top_p: float, temperature: float, u, out=None)
                             temperature, _dev(u, torch.float64, "u"), _dev(ids, torch.int32, "ids"),
                             _stream()), "qk_sample")
     return ids
+
+
+def qk_read_probe(buf, blocks=2048, out=None):
+    """Stream `buf` (a device tensor, a multiple of 16 bytes) through 128-bit
+    non-temporal loads; returns the per-workgroup XOR words.  Timing is the
+    caller's (a measurement helper, not an operation of the method)."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("qk_read_probe: buf must be a contiguous device tensor")
+    words = _out(out, (blocks,), torch.int32, buf)
+    _check(load().qk_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                _dev(words, torch.int32, "out"), blocks, _stream()), "qk_read_probe")
+    return words
 
 
 def qk_argmax(logits, out=None):

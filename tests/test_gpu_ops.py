@@ -458,3 +458,22 @@ def test_sampler_rejects_bad_top_k(gpu_lib):
     s = torch.cuda.current_stream().cuda_stream
     assert L.qk_sample(x.data_ptr(), 1, 10, 0, 0.9, 0.7, u.data_ptr(), o.data_ptr(), s) == qk.QK_EINVAL
     assert L.qk_sample(x.data_ptr(), 1, 10, 257, 0.9, 0.7, u.data_ptr(), o.data_ptr(), s) == qk.QK_EINVAL
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(2**20 + 48, 7), (16 * 1000, 2048), (16, 3)])
+def test_read_probe_reads_every_word_once(gpu_lib, nbytes, blocks):
+    """The bandwidth probe covers the buffer exactly once: the XOR of its
+    per-workgroup words equals the XOR of every 32-bit word of the buffer."""
+    qk = gpu_lib
+    say(f"qk_read_probe bytes={nbytes} blocks={blocks}")
+    rng = np.random.default_rng(nbytes + blocks)
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32).copy()).to("cuda")
+    out = qk.qk_read_probe(buf, blocks=blocks)
+    got = np.bitwise_xor.reduce(host(out).view(np.uint32))
+    want = np.bitwise_xor.reduce(words)
+    assert int(got) == int(want)
+    L = qk.load()
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.qk_read_probe(buf.data_ptr(), 24, out.data_ptr(), blocks, s) == qk.QK_ESHAPE
+    assert L.qk_read_probe(buf.data_ptr(), 16, out.data_ptr(), 0, s) == qk.QK_EINVAL
