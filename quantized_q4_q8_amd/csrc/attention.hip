@@ -258,22 +258,27 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 // from LDS, B = Q^T from registers), so that each lane's C registers are
 // exactly the B operand of O^T = V^T P^T (register v of key tile kt is key
 // step 4 kt + v): the probabilities never leave registers.  K and V are
-// staged in LDS as fp32 (exact widenings of fp16) with row strides HD + 2
-// and HD + 16, which keep the operand reads free of bank conflicts, and
-// double-buffered: the next chunk's rows are loaded into registers while
-// the current one is multiplied.
+// staged in LDS as fp32 (exact widenings of fp16), double-buffered: the
+// next chunk's rows are loaded into registers while the current one is
+// multiplied.  Within a row the values are permuted so that each lane's
+// operands are contiguous: K element d sits at (d % 4) HD/4 + d / 4 (a
+// lane reads the k-steps of its k index with 128-bit reads) and V element d
+// at (d % 16) HD/16 + d / 16 (one read gives a lane its value of every
+// output dim tile).  Row stride HD + 4 keeps both reads free of bank
+// conflicts on 32 banks.
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_flash_mfma(
+__global__ __launch_bounds__(256, 2) void k_attn_flash_mfma(
     const float* __restrict__ q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, float* __restrict__ out,
     int64_t o_ts, int8_t* __restrict__ oq, uint16_t* __restrict__ od) {
     constexpr int NS = HD / 4;     // k-steps of the score product (dims)
     constexpr int NDT = HD / 16;   // dim tiles of the output
-    constexpr int KS = HD + 2, VS = HD + 16;
+    constexpr int KS = HD + 4, VS = HD + 4;
+    constexpr int KQ = HD / 4, VQ = HD / 16;   // permuted row: K by k index, V by dim tile
     constexpr int KVPER = ACH * HD / 8 / 256;   // 8-value chunks of K (and of V) per thread
-    __shared__ float ks[2][ACH][KS];
-    __shared__ float vs[2][ACH][VS];
+    __shared__ __align__(16) float ks[2][ACH][KS];
+    __shared__ __align__(16) float vs[2][ACH][VS];
 
     const int G = (int)(nq / nkv);
     const int TQ = 64 / G;   // tokens per workgroup
@@ -334,13 +339,21 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
                 const int r = (i * 8) / HD, d = (i * 8) % HD;
                 const uint32_t kw[4] = {pk[e].x, pk[e].y, pk[e].z, pk[e].w};
                 const uint32_t vw[4] = {pv[e].x, pv[e].y, pv[e].z, pv[e].w};
+                float kf[8], vf[8];
 #pragma unroll
                 for (int f = 0; f < 4; ++f) {
-                    *reinterpret_cast<float2*>(&ks[buf][r][d + 2 * f]) =
-                        make_float2(h2f((uint16_t)(kw[f] & 0xFFFF)), h2f((uint16_t)(kw[f] >> 16)));
-                    *reinterpret_cast<float2*>(&vs[buf][r][d + 2 * f]) =
-                        make_float2(h2f((uint16_t)(vw[f] & 0xFFFF)), h2f((uint16_t)(vw[f] >> 16)));
+                    kf[2 * f] = h2f((uint16_t)(kw[f] & 0xFFFF));
+                    kf[2 * f + 1] = h2f((uint16_t)(kw[f] >> 16));
+                    vf[2 * f] = h2f((uint16_t)(vw[f] & 0xFFFF));
+                    vf[2 * f + 1] = h2f((uint16_t)(vw[f] >> 16));
                 }
+                // K: dims d + j (d % 8 == 0) go to (j % 4) KQ + d / 4 + j / 4
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    *reinterpret_cast<float2*>(&ks[buf][r][f * KQ + d / 4]) = make_float2(kf[f], kf[f + 4]);
+                // V: dims d + j go to ((d + j) % 16) VQ + d / 16
+#pragma unroll
+                for (int j = 0; j < 8; ++j) vs[buf][r][((d + j) % 16) * VQ + d / 16] = vf[j];
             }
         };
         if (kmax >= 0) {
@@ -360,12 +373,18 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) sc[kt] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
+            for (int s4 = 0; s4 < NS; s4 += 4) {   // four k-steps per 128-bit read
+                float4 kv[4];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const double a = (double)ks[cur][16 * kt + (lane & 15)][4 * st + kq];
-                    sc[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qT[st], sc[kt], 0, 0, 0);
-                }
+                for (int kt = 0; kt < 4; ++kt)
+                    kv[kt] = *reinterpret_cast<const float4*>(&ks[cur][16 * kt + (lane & 15)][kq * KQ + s4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) {
+                        const float a = i == 0 ? kv[kt].x : (i == 1 ? kv[kt].y : (i == 2 ? kv[kt].z : kv[kt].w));
+                        sc[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a, qT[s4 + i], sc[kt], 0, 0, 0);
+                    }
             }
             // mask, scale and the chunk's row max (the row's 64 keys sit in
             // this lane's 16 registers and lanes l ^ 16, l ^ 32, l ^ 48)
@@ -405,12 +424,22 @@ __global__ __launch_bounds__(256) void k_attn_flash_mfma(
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < 4; ++v) {
+                    // this lane's value of every dim tile: one read (NDT = 4
+                    // or 2 contiguous floats)
+                    const float* vr = &vs[cur][16 * kt + 4 * v + kq][(lane & 15) * VQ];
+                    float va[NDT];
+                    if constexpr (NDT == 4) {
+                        const float4 t = *reinterpret_cast<const float4*>(vr);
+                        va[0] = t.x; va[1] = t.y; va[2] = t.z; va[3] = t.w;
+                    } else {
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const double a = (double)vs[cur][16 * kt + 4 * v + kq][16 * dt + (lane & 15)];
-                        o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, sc[kt][v], o[dt], 0, 0, 0);
+                        for (int dt = 0; dt < NDT; ++dt) va[dt] = vr[dt];
                     }
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+                        o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[dt], sc[kt][v], o[dt], 0, 0, 0);
+                }
             if (more) sstore_kv(cur ^ 1);   // read two chunks ago, past the last barrier
             __syncthreads();
         }
