@@ -83,7 +83,10 @@ MM_CASES = [(5632, 2048, 1), (2048, 5632, 1), (5632, 2048, 8), (2048, 5632, 8),
             (384, 256, 16), (37, 704, 3), (100, 32, 2), (256, 2048, 9), (130, 2048, 33),
             (300, 6144, 130), (64, 256, 1), (4096, 6144, 2),
             # the MFMA path with K stages not filled (3 and 65 blocks), ragged rows and tokens
-            (70, 96, 33), (129, 2080, 65), (200, 32, 100)]
+            (70, 96, 33), (129, 2080, 65), (200, 32, 100),
+            # rows longer than one load step (K > 6144: 2 and 3 steps, the
+            # last one ragged)
+            (300, 8192, 4), (129, 12320, 1), (64, 8192, 8)]
 
 
 @pytest.mark.parametrize("n,k,m", MM_CASES)
@@ -115,6 +118,7 @@ def test_quantize_rowq_bit_exact(gpu_lib, bits, n, k):
 
 
 ROWQ_MM = [(5, 32, 1), (64, 2048, 3), (37, 704, 2), (2048, 6144, 1), (300, 8192, 4), (96, 256, 13),
+           (64, 8192, 13),
            (4096, 2048, 8)]
 
 
