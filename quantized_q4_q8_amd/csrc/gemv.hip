@@ -10,7 +10,9 @@
 // ..., reading a block's 16 nibble bytes with one 128-bit load (a wave reads
 // 1 KiB of a row contiguously) plus its fp16 scale.  All weight loads of a
 // step are issued before anything waits, so every wave has its whole share
-// in flight.  The activation columns are staged once per workgroup in LDS
+// in flight; when the share is one step, later column passes reuse the
+// registers instead of loading again.  The activation columns are staged
+// once per workgroup in LDS
 // (as Q8_0 codes and fp32 scales, either copied from the input or built by
 // a fused RMSNorm / Q8_0 prologue).  Nibbles are unpacked in registers with a
 // mask and a shift; v_dot4_i32_i8 forms the block's integer sum from the
