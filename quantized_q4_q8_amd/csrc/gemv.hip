@@ -256,7 +256,6 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     constexpr int RMAX = R;
     constexpr int P = rows_per_unit(EPI);
     static_assert(R % P == 0, "rows per wave must hold whole units");
-    constexpr int N = RMAX * M;              // sums per lane in the reduction
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int g = blockIdx.y;
@@ -304,13 +303,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     // loads stay in one basic block and issue in the order written.
     uint4 w[RMAX][U];
     uint16_t dwh[RMAX][U];   // fp16 block scales (Q4_0), converted where used
-    auto pass = [&](const int cc, auto first) __attribute__((always_inline)) {
+    auto pass = [&](const int cc, auto first, auto mt) __attribute__((always_inline)) {
+        constexpr int MM = decltype(mt)::value;   // columns of this pass
+        constexpr int NN = RMAX * MM;             // sums per lane in the reduction
         constexpr bool load_now = decltype(first)::value || KLOOP;
-        const int mc = nc - cc < M ? nc - cc : M;
+        const int mc = nc - cc < MM ? nc - cc : MM;
         float drs[RMAX];     // row scales (row-scaled formats), loaded by every pass
-        int xr[M];
+        int xr[MM];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
+        for (int m = 0; m < MM; ++m) {
             const int col = cc + m < nc ? cc + m : nc - 1;  // clamp: extra columns are discarded
             xr[m] = a.col_idx ? __builtin_amdgcn_readfirstlane(a.col_idx[c0 + col]) : c0 + col;
         }
@@ -353,7 +354,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             if constexpr (load_now) load_w(0);   // issued once the row has arrived
             stage_row<PRO, KC>(Rg, k, a.eps, red, lxq, lxd);
 #pragma unroll
-            for (int m = 1; m < M; ++m) {
+            for (int m = 1; m < MM; ++m) {
                 if (m >= mc) break;       // uniform over the workgroup
                 lds_barrier();            // `red` reused
                 load_row<PRO, KC>(Rg, a.xf + (int64_t)xr[m] * k, a.gamma, k);
@@ -362,7 +363,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         } else {
             // copy the Q8_0 columns into LDS: the first XREG chunks per thread
             // are loaded before the weights, the rest after
-            constexpr int XREG = M == 1 ? 2 : (M == 2 ? 3 : 6);   // up to K = 6144 staged early
+            constexpr int XREG = MM == 1 ? 2 : (MM == 2 ? 3 : 6);   // up to K = 6144 staged early
             // 16-byte chunks per column, chunk counts of the pass (32-bit:
             // K and the column count are small)
             const uint32_t c16 = (uint32_t)k / 16u, unb = (uint32_t)nb;
@@ -375,7 +376,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                 return cidx ? (int64_t)cidx[col] : (int64_t)col;
             };
             const uint32_t id = threadIdx.x < totd ? threadIdx.x : 0u;
-            const uint32_t md = col_of<M>(id, unb);
+            const uint32_t md = col_of<MM>(id, unb);
             uint16_t xdh;
             if constexpr (load_now && !KLOOP) {
             // (the loads are unconditional, so that none of them waits for
@@ -385,7 +386,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             for (int p = 0; p < XREG; ++p) {
                 uint32_t i = threadIdx.x + (uint32_t)p * 256u;
                 i = i < tot ? i : 0u;
-                const uint32_t m = col_of<M>(i, c16);
+                const uint32_t m = col_of<MM>(i, c16);
                 xs[p] = *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
             }
             xdh = a.xd[col_row(md) * nb + (id - md * unb)];
@@ -395,11 +396,11 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             for (int p = 0; p < XREG; ++p) {   // a thread past the end rewrites chunk 0 with itself
                 uint32_t i = threadIdx.x + (uint32_t)p * 256u;
                 i = i < tot ? i : 0u;
-                const uint32_t m = col_of<M>(i, c16);
+                const uint32_t m = col_of<MM>(i, c16);
                 *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) = xs[p];
             }
             for (uint32_t i = threadIdx.x + (uint32_t)XREG * 256u; i < tot; i += 256u) {
-                const uint32_t m = col_of<M>(i, c16);
+                const uint32_t m = col_of<MM>(i, c16);
                 *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) =
                     *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
             }
@@ -408,24 +409,24 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             if constexpr (load_now) load_w(0);
             if (FMT != FMT_Q4_0) load_rs();
             for (uint32_t i = threadIdx.x; i < tot; i += 256u) {
-                const uint32_t m = col_of<M>(i, c16);
+                const uint32_t m = col_of<MM>(i, c16);
                 *reinterpret_cast<uint4*>(lxq + (size_t)m * k + (i - m * c16) * 16u) =
                     *reinterpret_cast<const uint4*>(a.xq + col_row(m) * k + (i - m * c16) * 16u);
             }
             }
             lxd[id] = h2f(xdh);
             for (uint32_t i = threadIdx.x + 256u; i < totd; i += 256u) {
-                const uint32_t m = col_of<M>(i, unb);
+                const uint32_t m = col_of<MM>(i, unb);
                 lxd[i] = h2f(a.xd[col_row(m) * nb + (i - m * unb)]);
             }
         }
         lds_barrier();
 
-        double acc[RMAX][M];
+        double acc[RMAX][MM];
 #pragma unroll
         for (int j = 0; j < RMAX; ++j)
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[j][m] = 0.0;
+            for (int m = 0; m < MM; ++m) acc[j][m] = 0.0;
 
         for (int64_t b0 = 0; b0 < nb; b0 += (int64_t)WAVE * U) {
             if (KLOOP && b0 > 0) load_w(b0);
@@ -434,7 +435,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                 const int64_t b = b0 + u * WAVE + lane;
                 if (b >= nb) break;
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
+                for (int m = 0; m < MM; ++m) {
                     const int8_t* xp = lxq + (size_t)m * k + b * QBLK;
                     const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
                     const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 16);
@@ -459,16 +460,16 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         }
 
         // all row/column sums of the wave at once; value index r = m * RMAX + j
-        double v[N];
+        double v[NN];
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int m = 0; m < MM; ++m)
 #pragma unroll
             for (int j = 0; j < RMAX; ++j) v[m * RMAX + j] = acc[j][m];
-        const int base = row_sums<N>(v, lane);
+        const int base = row_sums<NN>(v, lane);
         // this lane's sum (index r) and, for two-row units, the unit's other
         // row (index r ^ 1: the same lane when a row holds several sums, else
         // the lane that differs in the last halving bit)
-        constexpr int NV = N >= 4 ? N / 4 : 1;
+        constexpr int NV = NN >= 4 ? NN / 4 : 1;
         const int kk = NV > 1 ? (lane & 15) : 0;
         double s = v[0], s2 = 0.0;
 #pragma unroll
@@ -481,7 +482,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                 for (int q = 1; q < NV; ++q)
                     if ((kk ^ 1) == q) s2 = v[q];
             } else {
-                s2 = __shfl_xor(s, N == 4 ? 16 : 32, WAVE);
+                s2 = __shfl_xor(s, NN == 4 ? 16 : 32, WAVE);
             }
         }
         const int r = base + kk;
@@ -496,7 +497,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             s *= (double)d1;
             if (P == 2) s2 *= (double)d2;
         }
-        constexpr int OWN = N >= 4 ? 16 : (N == 2 ? 32 : 64);   // lanes sharing one row's sums
+        constexpr int OWN = NN >= 4 ? 16 : (NN == 2 ? 32 : 64);   // lanes sharing one row's sums
         const bool owner = (NV > 1 ? kk < NV : (lane & (OWN - 1)) == 0) && rvalid(j) && cc + m < nc;
         const int64_t row = prow(j);
         const int64_t ocol = c0 + cc + m;
@@ -570,13 +571,26 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             }
         }
     };
+    using MFull = std::integral_constant<int, M>;
     if constexpr (KLOOP || PRO != PRO_NONE) {
         // (fused-prologue kernels keep loading per pass: their own row
         // staging must come first, and their passes are rare)
-        for (int cc = 0; cc < nc; cc += M) pass(cc, std::true_type{});
+        for (int cc = 0; cc < nc; cc += M) pass(cc, std::true_type{}, MFull{});
     } else {
-        pass(0, std::true_type{});
-        for (int cc = M; cc < nc; cc += M) pass(cc, std::false_type{});
+        // A two-column kernel runs a pass with one column left (an expert
+        // with an odd token count) as a one-column body: the dots and the
+        // scaling of a padding column are not done.
+        auto run = [&](const int cc, auto first) __attribute__((always_inline)) {
+            if constexpr (M == 2) {
+                if (nc - cc == 1) {   // uniform over the workgroup
+                    pass(cc, first, std::integral_constant<int, 1>{});
+                    return;
+                }
+            }
+            pass(cc, first, MFull{});
+        };
+        run(0, std::true_type{});
+        for (int cc = M; cc < nc; cc += M) run(cc, std::false_type{});
     }
 }
 
