@@ -176,6 +176,32 @@ __global__ __launch_bounds__(256) void k_embed(const float* __restrict__ table, 
     for (int64_t i = threadIdx.x; i < hidden; i += 256) x[r * hidden + i] = ok ? src[i] : 0.0f;
 }
 
+// The same for 16-byte aligned rows of a multiple of 4 values: each thread
+// issues its (up to) four 128-bit loads together, with indexes clamped into
+// the row, before storing any, so a row up to 4096 values costs one memory
+// round trip after the id.
+__global__ __launch_bounds__(256) void k_embed4(const float4* __restrict__ table, int64_t vocab,
+                                                int64_t h4, const int32_t* __restrict__ ids,
+                                                float4* __restrict__ x) {
+    const int64_t r = blockIdx.x;
+    const int id = ids[r];
+    const bool ok = id >= 0 && id < vocab;
+    const float4* src = table + (int64_t)(ok ? id : 0) * h4;
+    for (int64_t i0 = 0; i0 < h4; i0 += 4 * 256) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * 256 + threadIdx.x;
+            v[u] = src[i < h4 ? i : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * 256 + threadIdx.x;
+            if (i < h4) x[r * h4 + i] = ok ? v[u] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+}
+
 // ----------------------------------------------------------------- argmax
 // One workgroup per row; (value, index) pairs reduce with ties to the lower
 // index, NaN never wins.
@@ -265,8 +291,13 @@ extern "C" int qk_embed_lookup(const float* table, int64_t vocab, int64_t hidden
     QK_REQUIRE(vocab > 0 && hidden > 0 && n >= 0, QK_EINVAL);
     if (n == 0) return QK_OK;
     QK_REQUIRE(table && ids && x, QK_EINVAL);
-    hipLaunchKernelGGL(k_embed, dim3((unsigned)n), dim3(256), 0, (hipStream_t)stream, table,
-                       vocab, hidden, ids, x);
+    if (hidden % 4 == 0 && QK_ALIGNED(table, 16) && QK_ALIGNED(x, 16))
+        hipLaunchKernelGGL(k_embed4, dim3((unsigned)n), dim3(256), 0, (hipStream_t)stream,
+                           reinterpret_cast<const float4*>(table), vocab, hidden / 4, ids,
+                           reinterpret_cast<float4*>(x));
+    else
+        hipLaunchKernelGGL(k_embed, dim3((unsigned)n), dim3(256), 0, (hipStream_t)stream, table,
+                           vocab, hidden, ids, x);
     return qk_launch_status();
 }
 

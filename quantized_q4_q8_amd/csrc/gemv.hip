@@ -614,10 +614,24 @@ __global__ __launch_bounds__(256) void k_argmax_partials(const float* __restrict
     const int64_t c = blockIdx.x;
     float bv = -INFINITY;
     int bi = INT32_MAX;
-    for (int64_t i = threadIdx.x; i < nparts; i += 256) {
-        const float v = pv[c * nparts + i];
-        const int j = pi[c * nparts + i];
-        if (v > bv || (v == bv && j < bi)) { bv = v; bi = j; }
+    // eight partials per thread per round, their loads issued together
+    // (indexes clamped into the column; the extra ones are not compared)
+    for (int64_t i0 = 0; i0 < nparts; i0 += 8 * 256) {
+        float v[8];
+        int j[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = i0 + u * 256 + threadIdx.x;
+            const int64_t ic = i < nparts ? i : 0;
+            v[u] = pv[c * nparts + ic];
+            j[u] = pi[c * nparts + ic];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (i0 + u * 256 + threadIdx.x < nparts && (v[u] > bv || (v[u] == bv && j[u] < bi))) {
+                bv = v[u];
+                bi = j[u];
+            }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
