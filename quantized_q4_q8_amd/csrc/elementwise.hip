@@ -65,11 +65,87 @@ __global__ __launch_bounds__(256) void k_rmsnorm_q8(const float* __restrict__ x,
     }
 }
 
+// Rows up to KC * 2048 values: each lane takes 8 consecutive values of every
+// 2048-value chunk, and the row and gamma are loaded once, all at once
+// (unconditional loads, indexes clamped into the row), into registers; the
+// sum of squares, the normalization and the Q8_0 codes come from there.
+// The lane mapping and the order of the fp64 sums are those of the GEMV's
+// fused prologue, so both give the same sum of squares for a row.
+template <int KC>
+__global__ __launch_bounds__(256) void k_rmsnorm_q8_reg(const float* __restrict__ x,
+                                                        const float* __restrict__ gamma,
+                                                        int64_t dim, float eps,
+                                                        float* __restrict__ y,
+                                                        int8_t* __restrict__ xq,
+                                                        uint16_t* __restrict__ xd) {
+    __shared__ double red[4];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * dim;
+    float xv[KC][8], gv[KC][8];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        int64_t i = (int64_t)c * 2048 + threadIdx.x * 8;
+        i = i < dim ? i : 0;
+        const float4 a = *reinterpret_cast<const float4*>(xr + i);
+        const float4 b = *reinterpret_cast<const float4*>(xr + i + 4);
+        const float4 ga = *reinterpret_cast<const float4*>(gamma + i);
+        const float4 gb = *reinterpret_cast<const float4*>(gamma + i + 4);
+        xv[c][0] = a.x; xv[c][1] = a.y; xv[c][2] = a.z; xv[c][3] = a.w;
+        xv[c][4] = b.x; xv[c][5] = b.y; xv[c][6] = b.z; xv[c][7] = b.w;
+        gv[c][0] = ga.x; gv[c][1] = ga.y; gv[c][2] = ga.z; gv[c][3] = ga.w;
+        gv[c][4] = gb.x; gv[c][5] = gb.y; gv[c][6] = gb.z; gv[c][7] = gb.w;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        const bool in = (int64_t)c * 2048 + threadIdx.x * 8 < dim;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double v = in ? (double)xv[c][e] : 0.0;
+            ss = fma(v, v, ss);
+        }
+    }
+    ss = group_sum<WAVE>(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double total = red[0] + red[1] + red[2] + red[3];
+    const double denom = sqrt(total / (double)dim + (double)eps);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        if ((int64_t)c * 2048 >= dim) break;   // uniform over the workgroup
+        const int64_t i = (int64_t)c * 2048 + threadIdx.x * 8;
+        const bool live = i < dim;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = live ? (float)((double)xv[c][e] / denom * (double)gv[c][e]) : 0.0f;
+        if (y && live) {
+            *reinterpret_cast<float4*>(y + row * dim + i) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(y + row * dim + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        if (xq) {
+            uint32_t lo, hi;
+            float d;
+            q8_quad(v, lo, hi, d);
+            if (live) {
+                *reinterpret_cast<uint2*>(xq + row * dim + i) = make_uint2(lo, hi);
+                if ((threadIdx.x & 3) == 0) xd[row * (dim / QBLK) + i / QBLK] = f2h(d);
+            }
+        }
+    }
+}
+
 int launch_rmsnorm_q8(const float* x, const float* gamma, int64_t rows, int64_t dim, float eps,
                       float* y, int8_t* xq, uint16_t* xd, hipStream_t s) {
     if (rows == 0) return QK_OK;
-    hipLaunchKernelGGL(k_rmsnorm_q8, dim3((unsigned)rows), dim3(256), 0, s, x, gamma, dim, eps, y,
-                       xq, xd);
+    const dim3 grid((unsigned)rows), block(256);
+    if (dim <= 2048)
+        hipLaunchKernelGGL(k_rmsnorm_q8_reg<1>, grid, block, 0, s, x, gamma, dim, eps, y, xq, xd);
+    else if (dim <= 4096)
+        hipLaunchKernelGGL(k_rmsnorm_q8_reg<2>, grid, block, 0, s, x, gamma, dim, eps, y, xq, xd);
+    else if (dim <= 6144)
+        hipLaunchKernelGGL(k_rmsnorm_q8_reg<3>, grid, block, 0, s, x, gamma, dim, eps, y, xq, xd);
+    else
+        hipLaunchKernelGGL(k_rmsnorm_q8, grid, block, 0, s, x, gamma, dim, eps, y, xq, xd);
     return qk_launch_status();
 }
 
