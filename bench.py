@@ -6,8 +6,8 @@ Default workload: TinyLLaMA-1.1B-shaped greedy decode (22 layers, hidden
 from N(0, 0.02), fp16 KV cache prefilled with N(0, 1) to context 2048).  One
 step is the workload's full 128-token greedy decode (positions 2048..2175):
 per token embedding, 22 decoder layers, final RMSNorm, LM head and argmax.
-Each token's kernels are captured once in a HIP graph and replayed; inputs
-are resident in HBM before timing starts.
+The step's kernels (all 128 tokens, back to back) are captured once in a HIP
+graph and replayed; inputs are resident in HBM before timing starts.
 
 Prints one JSON line: throughput (tokens/s), the dominant kernel's HBM
 roofline (its average duration from HIP events on its stream), and the CPU
@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--kernel-rounds", type=int, default=20)
+    ap.add_argument("--graph", choices=["token", "step"], default="step",
+                    help="decode capture: one HIP graph per token position, or the whole "
+                         "step's tokens in one graph")
     ap.add_argument("--decode-tokens", type=int, default=128,
                     help="tokens per step; only for short profiling runs (the workload is 128)")
     return ap.parse_args()
@@ -183,7 +186,8 @@ def run_decode(args, long_context: bool = False):
     dec, first, host = build_decoder(spec, want_cpu)
     dev = dec.device
 
-    # -- one HIP graph per decode position (positions 2048 .. 2175)
+    # -- the decode positions (2048 .. 2175) captured in one HIP graph (or
+    #    one graph per position with --graph token)
     dec.reserve(1)
     bufs = dec.step_buffers(1)
     ids = torch.tensor(first, dtype=torch.int32, device=dev)
@@ -195,13 +199,20 @@ def run_decode(args, long_context: bool = False):
     torch.cuda.synchronize()
     t0 = time.time()
     graphs = []
-    for j in range(steps_per_run):
+    if args.graph == "step":   # the step's tokens back to back in one graph
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
-            dec.step(ids, positions[j], seq, bufs)
+            for j in range(steps_per_run):
+                dec.step(ids, positions[j], seq, bufs)
         graphs.append(gr)
+    else:
+        for j in range(steps_per_run):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                dec.step(ids, positions[j], seq, bufs)
+            graphs.append(gr)
     torch.cuda.synchronize()
-    log(f"captured {len(graphs)} decode graphs in {time.time() - t0:.1f}s")
+    log(f"captured {len(graphs)} decode graph(s) for {steps_per_run} tokens in {time.time() - t0:.1f}s")
 
     def one_run():
         for gr in graphs:
