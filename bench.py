@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--graph", choices=["token", "step"], default="step",
                     help="decode capture: one HIP graph per token position, or the whole "
                          "step's tokens in one graph")
+    ap.add_argument("--no-arena", action="store_true",
+                    help="decode: keep each weight in its own allocation instead of one arena "
+                         "in step order")
     ap.add_argument("--decode-tokens", type=int, default=128,
                     help="tokens per step; only for short profiling runs (the workload is 128)")
     return ap.parse_args()
@@ -185,6 +188,9 @@ def run_decode(args, long_context: bool = False):
     want_cpu = not args.no_cpu_baseline
     dec, first, host = build_decoder(spec, want_cpu)
     dev = dec.device
+    if not args.no_arena:   # all weights in one allocation, in the order the step reads them
+        dec.pack()
+        torch.cuda.synchronize()
 
     # -- the decode positions (2048 .. 2175) captured in one HIP graph (or
     #    one graph per position with --graph token)

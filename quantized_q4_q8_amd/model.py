@@ -78,6 +78,30 @@ class Decoder:
         self.head_ws = Workspace()
         self.device = device
 
+    def pack(self, align: int = 4096) -> None:
+        """Move every layer's weights and the LM head into one device
+        allocation, in the order the step reads them (each slice aligned to
+        `align` bytes); the old tensors are released."""
+        fields = ["w_qkv_q", "w_qkv_d", "w_o_q", "w_o_d", "w_gate_up_q", "w_gate_up_d",
+                  "w_down_q", "w_down_d", "gamma_attn", "gamma_ffn"]
+        tensors = [getattr(lw, f) for lw in self.layers for f in fields] + [self.lm_q, self.lm_d]
+        sizes = [t.numel() * t.element_size() for t in tensors]
+        offs, o = [], 0
+        for n in sizes:
+            offs.append(o)
+            o += (n + align - 1) // align * align
+        arena = torch.empty(o, dtype=torch.uint8, device=self.device)
+        views = []
+        for t, off, n in zip(tensors, offs, sizes):
+            v = arena[off:off + n].view(t.dtype).view(t.shape)
+            v.copy_(t)
+            views.append(v)
+        it = iter(views)
+        self.layers = [LayerWeights(*[next(it) for _ in fields]) for _ in self.layers]
+        self.lm_q, self.lm_d = next(it), next(it)
+        self.structs = [lw.struct() for lw in self.layers]
+        self.arena = arena
+
     def reserve(self, tokens: int) -> None:
         """Size the workspace for calls of up to `tokens` tokens (before graph capture)."""
         self.ws.reserve(qk_layer_workspace(self.cfg, tokens), self.device)

@@ -79,11 +79,15 @@ def oracle_forward(hm, ids, pos, seq, kv):
 
 def test_decode_tinyllama_shape_teacher_forced(gpu_lib):
     """22-layer decode from a 2048-row fp16 KV prefill: logits within 1e-2 and
-    greedy tokens matching the oracle on every step (teacher-forced)."""
+    greedy tokens matching the oracle on every step (teacher-forced).  The
+    weights are packed into one arena first, as the benchmark holds them."""
     spec = W.DECODE
     g, L, cap, ctx = spec["geometry"], spec["layers"], spec["cap"], spec["context"]
     say("decode: building the 22-layer model")
     dec, hm = build(spec, 1)
+    dec.pack()
+    assert all(lw.w_gate_up_q.untyped_storage().data_ptr() == dec.arena.untyped_storage().data_ptr()
+               for lw in dec.layers)
     kv = []
     for li in range(L):
         kc, vc = W.kv_prefill_f16(spec["seed"], li, g.n_kv_heads, cap, g.head_dim, ctx)
