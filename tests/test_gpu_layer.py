@@ -178,7 +178,10 @@ def check_routing(sel_g, w_g, sel_o, w_o, logits):
         assert srt[k - 1] - srt[k] < 1e-5, f"token {t}: selection differs without a near tie"
 
 
-@pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (1, 128, 8, 32, 1)])
+@pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (1, 128, 8, 32, 1),
+                                       # 1600 pairs: the grouping's second chunk of 1024,
+                                       # about 100 tokens per expert (passes of 8 columns)
+                                       (200, 64, 16, 32, 8)])
 def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     qk = gpu_lib
     say(f"moe_route_and_apply T={T} H={H} E={E} F={F} k={k}")
