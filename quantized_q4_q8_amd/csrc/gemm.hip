@@ -90,8 +90,13 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
 
     // ---- global -> register staging (per thread and step: A_PER activation
     // chunks, B_PER weight chunks, one activation scale, DB_PER weight scales)
+    // The fp16 scales are loaded from clamped indexes with no branch and kept
+    // as raw bits plus a validity flag until sstore: a conversion here would
+    // make the wave wait for every load of the stage before the MFMAs of the
+    // current one could start.
     uint4 ra[A_PER], rb[B_PER];
-    float rda, rdb[DB_PER];
+    uint16_t rdah, rdbh[DB_PER];
+    bool rda_ok, rdb_ok[DB_PER];
     auto gload = [&](int64_t kb0) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
@@ -118,14 +123,16 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
             const int bb = tid / BT, r = tid % BT;   // activation scales [KB][BT]
             const int64_t b = kb0 + bb;
             const int64_t t = t0 + r;
-            rda = (t < m && b < nb) ? h2f(a.xd[t * nb + b]) : 0.0f;
+            rda_ok = t < m && b < nb;
+            rdah = a.xd[rda_ok ? t * nb + b : 0];
         }
 #pragma unroll
         for (int i = 0; i < DB_PER; ++i) {
             const int idx = tid + NT * i;            // weight scales [KB][BR]
             const int bb = idx / BR, r = idx % BR;
             const int64_t b = kb0 + bb;
-            rdb[i] = (prow_valid(r) && b < nb) ? h2f(a.wd[prow_of(r) * nb + b]) : 0.0f;
+            rdb_ok[i] = prow_valid(r) && b < nb;
+            rdbh[i] = a.wd[rdb_ok[i] ? prow_of(r) * nb + b : 0];
         }
     };
     auto sstore = [&](Stage& s) {
@@ -144,11 +151,11 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
             *reinterpret_cast<uint4*>(s.b + pr * STRIDE + bb * QBLK) = nib_codes(rb[i], 0);
             *reinterpret_cast<uint4*>(s.b + pr * STRIDE + bb * QBLK + 16) = nib_codes(rb[i], 4);
         }
-        s.da[tid / BT][tid % BT] = (double)rda;
+        s.da[tid / BT][tid % BT] = rda_ok ? (double)h2f(rdah) : 0.0;
 #pragma unroll
         for (int i = 0; i < DB_PER; ++i) {
             const int idx = tid + NT * i;
-            s.db[idx / BR][idx % BR] = rdb[i];
+            s.db[idx / BR][idx % BR] = rdb_ok[i] ? h2f(rdbh[i]) : 0.0f;
         }
     };
 
