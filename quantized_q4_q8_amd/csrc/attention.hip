@@ -291,26 +291,40 @@ __global__ __launch_bounds__(256, 2) void k_attn_flash_mfma(
     const int kq = lane >> 4;                          // lane's k index (0..3)
     const double rscale = sqrt((double)HD);
 
+    // The tile's sequence ids and positions, read once into LDS: the scans
+    // below would otherwise wait for one load after another.
+    __shared__ int tseq[64], tpos[64];
+    if (tid < ntile) {
+        tseq[tid] = seq[t0 + tid];
+        tpos[tid] = pos[t0 + tid];
+    }
+    __syncthreads();
+
     for (int i0 = 0; i0 < ntile;) {   // runs of one sequence (uniform)
-        const int s0 = seq[t0 + i0];
+        const int s0 = tseq[i0];
         int i1 = i0 + 1;
-        while (i1 < ntile && seq[t0 + i1] == s0) ++i1;
+        while (i1 < ntile && tseq[i1] == s0) ++i1;
         // row limits: the last ring row attended (-1: nothing)
         int kmax = -1;
         for (int i = i0; i < i1; ++i) {
-            const int p = pos[t0 + i];
+            const int p = tpos[i];
             if (p >= 0) kmax = max(kmax, (int)min((int64_t)p, cap - 1));
         }
         const bool mine = qvalid && qi >= i0 && qi < i1;
         int pl = -1;
         if (mine) {
-            const int p = pos[t0 + qi];
+            const int p = tpos[qi];
             pl = p >= 0 ? (int)min((int64_t)p, cap - 1) : -1;
         }
+        // q loads from a clamped index (row t0, head g G when the lane has no
+        // query row), all issued before any of them is used
+        const int64_t qoff = mine ? (t0 + qi) * q_ts + (g * G + qh) * HD : t0 * q_ts + g * G * HD;
         double qT[NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-            qT[st] = mine ? (double)q[(t0 + qi) * q_ts + (g * G + qh) * HD + 4 * st + kq] : 0.0;
+        for (int st = 0; st < NS; ++st) {
+            const float qv = q[qoff + 4 * st + kq];
+            qT[st] = mine ? (double)qv : 0.0;
+        }
 
         double m = -INFINITY, lsum = 0.0;
         v4d o[NDT];
