@@ -213,6 +213,24 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
 
     // ---- epilogue: lane j owns weight column lds_col(cb); register v is
     // token row 8 * (v / 4) + 4 * h + (v % 4) of the wave's 32-token tile.
+    // The residual values are all read (from clamped indexes) before the
+    // first store: y may equal residual, so the compiler could not move a
+    // load above an earlier store, and each load would wait on its own.
+    // Every element is read and then written by the same lane.
+    float rv[2][16];
+    if (EPI == EPI_STORE && a.residual) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t t = t0 + wt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+            const int64_t tc = t < m ? t : m - 1;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int pr = lds_col(cb);
+                const int64_t r = prow_valid(pr) ? prow_of(pr) : 0;
+                rv[cb][v] = a.residual[tc * a.ldr + r];
+            }
+        }
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int64_t t = t0 + wt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
                 if (!prow_valid(pr)) continue;
                 const int64_t r = prow_of(pr);
                 float val = (float)acc[cb][v];
-                if (a.residual) val = a.residual[t * a.ldr + r] + val;
+                if (a.residual) val = rv[cb][v] + val;
                 a.y[t * a.ldy + r] = val;
             }
         } else {
