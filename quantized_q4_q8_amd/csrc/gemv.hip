@@ -184,9 +184,18 @@ __device__ __forceinline__ void stage_row(const RowRegs<KC>& R, int64_t k, float
 // b5 * N/2 + b4 * N/4 + k, k < max(N/4, 1) (for N < 4 the index is b5 when
 // N = 2, 0 when N = 1).  The order of additions is fixed, so the result is
 // deterministic.
+// The first value index whose sums row_sums leaves in the 16-lane row of
+// `lane` (see row_sums).
+template <int N>
+__device__ __forceinline__ int row_sums_base(int lane) {
+    int base = 0;
+    if (N >= 2 && (lane & 32) != 0) base += N / 2;
+    if (N >= 4 && (lane & 16) != 0) base += N / 4;
+    return base;
+}
+
 template <int N>
 __device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
-    int base = 0;
     if (N >= 2) {
         constexpr int h = N / 2;
         const bool up = (lane & 32) != 0;
@@ -196,7 +205,6 @@ __device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
             const double keep = up ? v[i + h] : v[i];
             v[i] = keep + __shfl_xor(send, 32, WAVE);
         }
-        base += up ? h : 0;
     }
     if (N >= 4) {
         constexpr int h = N / 4;
@@ -207,7 +215,6 @@ __device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
             const double keep = up ? v[i + h] : v[i];
             v[i] = keep + __shfl_xor(send, 16, WAVE);
         }
-        base += up ? h : 0;
     }
     constexpr int NV = N >= 4 ? N / 4 : 1;
 #pragma unroll
@@ -216,7 +223,7 @@ __device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
         if (N <= 2) v[k] += __shfl_xor(v[k], 16, WAVE);
         v[k] = group_sum<16>(v[k]);
     }
-    return base;
+    return row_sums_base<N>(lane);
 }
 
 // Physical rows per output unit: SwiGLU units are (gate row, up row), QKV
@@ -347,6 +354,21 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             for (int j = 0; j < RMAX; ++j) drs[j] = FMT != FMT_Q4_0 ? wr[rvalid(j) ? prow(j) : 0] : 0.0f;
         };
 
+        // QKV epilogue inputs of the sum this lane will own (its column's
+        // position and its RoPE pair's base frequency), read before the
+        // activation row so that they arrive while the row is awaited rather
+        // than after the reductions.  Lanes that own no sum read column c0 + cc
+        // and pair 0 and discard them.
+        int qpos = 0;
+        double qtheta = 0.0;
+        if constexpr (EPI == EPI_QKV) {
+            constexpr int NVR = NN >= 4 ? NN / 4 : 1;
+            const int rr = row_sums_base<NN>(lane) + (NVR > 1 ? (lane & 15) : 0);
+            const bool ok = rr < NN && cc + rr / RMAX < nc;
+            qpos = a.pos[c0 + cc + (ok ? rr / RMAX : 0)];
+            const int64_t row0 = 2 * (unit0 + (ok ? rr % RMAX : 0) / 2);
+            qtheta = theta[(row0 % a.hd) / 2];
+        }
         if (cc > 0) lds_barrier();   // the previous pass finished reading LDS
         if (PRO != PRO_NONE) {
             RowRegs<KC> Rg;
@@ -517,10 +539,10 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
                     // RoPE angle of this pair in fp64, computed here where the
                     // weight registers are free
                     const int64_t row0 = 2 * unit;
-                    const int p = a.pos[ocol];
+                    const int p = qpos;   // a.pos[ocol], read at the start of the pass
                     double c = 1.0, sn = 0.0;
                     if (row0 < a.q_rows + a.kv_rows)
-                        rope_sincos((double)p * theta[(row0 % a.hd) / 2], sn, c);
+                        rope_sincos((double)p * qtheta, sn, c);
                     const double x1 = (double)(float)s, x2 = (double)(float)s2;
                     if (row0 < a.q_rows) {
                         a.q_out[ocol * a.q_rows + row0] = (float)(x1 * c - x2 * sn);
