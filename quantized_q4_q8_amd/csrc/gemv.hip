@@ -369,6 +369,17 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
             const int64_t row0 = 2 * (unit0 + (ok ? rr % RMAX : 0) / 2);
             qtheta = theta[(row0 % a.hd) / 2];
         }
+        // Likewise the residual that this lane adds in the store epilogue.
+        // y may equal the residual: each element is read and then written by
+        // the lane that owns its sum, and no two lanes own one.
+        float rres = 0.0f;
+        if (EPI == EPI_STORE && a.residual) {
+            constexpr int NVR = NN >= 4 ? NN / 4 : 1;
+            const int rr = row_sums_base<NN>(lane) + (NVR > 1 ? (lane & 15) : 0);
+            const int rm = rr / RMAX, rj = rr % RMAX;
+            const bool ok = rr < NN && rvalid(rj) && cc + rm < nc;
+            rres = a.residual[(c0 + cc + (ok ? rm : 0)) * a.ldr + (ok ? prow(rj) : 0)];
+        }
         if (cc > 0) lds_barrier();   // the previous pass finished reading LDS
         if (PRO != PRO_NONE) {
             RowRegs<KC> Rg;
@@ -527,7 +538,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         if (EPI == EPI_STORE) {
             if (owner) {
                 float o = (float)s;
-                if (a.residual) o = a.residual[ocol * a.ldr + row] + o;
+                if (a.residual) o = rres + o;   // read at the start of the pass
                 a.y[ocol * a.ldy + row] = o;
             }
         } else if (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
