@@ -58,7 +58,13 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
     const int64_t c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int G = (int)(nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // position and sequence read together, before the early exits, so that
+    // the two small loads cost one round trip (the empty asm takes both
+    // values, which keeps the compiler from moving the second load past the
+    // exits)
     const int p = pos[t];
+    const int sq = seq[t];
+    asm volatile("" ::"s"(p), "s"(sq));
     if (p < 0) return;   // negative positions read nothing
     const int64_t pe = min((int64_t)p, cap - 1);   // last ring row attended
     const int64_t r0 = c * ACH;
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
     static_assert(ACH * HD / 8 <= 512, "one K/V piece per thread");
     const int iq = tid < G * HD ? tid : 0;
     const float qv = q[t * q_ts + (g * G) * HD + iq];
-    const int64_t cbase = (((int64_t)seq[t] * nkv + g) * cap + r0) * HD;
+    const int64_t cbase = (((int64_t)sq * nkv + g) * cap + r0) * HD;
     const int i = tid < ACH * HD / 8 ? tid : 0;
     const int r = (i * 8) / HD, d = (i * 8) % HD;
     const int64_t roff = (int64_t)(r < rows ? r : 0) * HD + d;
