@@ -267,6 +267,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
     const int wave = threadIdx.x / WAVE;
     const int g = blockIdx.y;
     constexpr int upw = R / P;               // units per wave
+    // One-column kernels (decode): the kernel arguments that the set-up
+    // below reads, fetched in one round.  The empty asm takes them all, so
+    // the compiler issues their loads together instead of one wait per
+    // branch that reads one.  (Not for several columns: there the asm turns
+    // the grouped path's column-offset read into a vector load, which
+    // measured slower on the MoE layer.)
+    if constexpr (M == 1)
+        asm volatile("" ::"s"(a.col_off), "s"(a.m), "s"(a.n), "s"(a.k), "s"(a.wq), "s"(a.wd),
+                     "s"(a.ffn), "s"(PRO != PRO_NONE ? (const void*)a.xf : (const void*)a.xq));
 
     const int64_t nunits = (EPI == EPI_SWIGLU) ? a.ffn : (EPI == EPI_QKV ? a.n / 2 : a.n);
     const int64_t wg_unit0 = (int64_t)blockIdx.x * 4 * upw;
