@@ -194,24 +194,25 @@ def run_decode(args, long_context: bool = False):
 
     # -- the decode positions (2048 .. 2175) captured in one HIP graph (or
     #    one graph per position with --graph token)
-    dec.reserve(1)
-    bufs = dec.step_buffers(1)
-    ids = torch.tensor(first, dtype=torch.int32, device=dev)
-    bufs["next"] = ids                         # argmax writes the next input token in place
     seq = torch.zeros(1, dtype=torch.int32, device=dev)
     positions = [torch.tensor([spec["context"] + j], dtype=torch.int32, device=dev)
                  for j in range(steps_per_run)]
-    dec.step(ids, positions[0], seq, bufs)     # eager warm-up (first launches)
-    torch.cuda.synchronize()
     t0 = time.time()
     graphs = []
-    if args.graph == "step":   # the step's tokens back to back in one graph
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for j in range(steps_per_run):
-                dec.step(ids, positions[j], seq, bufs)
-        graphs.append(gr)
+    if args.graph == "step":
+        # the step's tokens back to back in one graph: token j reads ids[j],
+        # its argmax writes ids[j + 1]
+        ids = torch.zeros(steps_per_run + 1, dtype=torch.int32, device=dev)
+        ids[0] = int(first[0])
+        logits = torch.empty((1, spec["vocab"]), dtype=torch.float32, device=dev)
+        graphs.append(dec.capture_decode(ids, positions, seq, logits, ids[1:]))
     else:
+        dec.reserve(1)
+        bufs = dec.step_buffers(1)
+        ids = torch.tensor(first, dtype=torch.int32, device=dev)
+        bufs["next"] = ids                     # argmax writes the next input token in place
+        dec.step(ids, positions[0], seq, bufs)  # eager warm-up (first launches)
+        torch.cuda.synchronize()
         for j in range(steps_per_run):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
@@ -224,7 +225,8 @@ def run_decode(args, long_context: bool = False):
         for gr in graphs:
             gr.replay()
 
-    ids.fill_(int(first[0]))
+    if args.graph != "step":
+        ids.fill_(int(first[0]))
     for _ in range(args.warmup):
         one_run()
     torch.cuda.synchronize()

@@ -123,6 +123,30 @@ class Decoder:
         return qk_lm_head(x, self.gamma_final, self.s.eps, self.lm_q, self.lm_d,
                           logits=b.get("logits"), next_ids=b.get("next"), ws=self.head_ws)
 
+    def capture_decode(self, ids: torch.Tensor, positions: list[torch.Tensor], seq: torch.Tensor,
+                       logits: torch.Tensor, next_ids: torch.Tensor) -> torch.cuda.CUDAGraph:
+        """Capture len(positions) one-token decode steps back to back in one
+        HIP graph.  Step j reads its token from ids[j], runs at positions[j],
+        writes its logits to logits[j % logits.shape[0]] and its greedy token
+        to next_ids[j].  Greedy decoding passes next_ids = ids[1:] (each
+        step's argmax is the next step's input); teacher forcing passes ids
+        filled beforehand and a separate next_ids."""
+        n = len(positions)
+        assert ids.numel() >= n and next_ids.numel() >= n
+        self.reserve(1)
+        x = torch.empty((1, self.s.hidden), dtype=torch.float32, device=self.device)
+        rows = logits.shape[0]
+        # first launches outside the capture
+        self.step(ids[0:1], positions[0], seq, dict(x=x, logits=logits[0:1], next=next_ids[0:1]))
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for j in range(n):
+                r = j % rows
+                self.step(ids[j:j + 1], positions[j], seq,
+                          dict(x=x, logits=logits[r:r + 1], next=next_ids[j:j + 1]))
+        return gr
+
     def step_buffers(self, tokens: int) -> dict:
         """Preallocated buffers so that `step` allocates nothing (graph capture)."""
         dev, H, V = self.device, self.s.hidden, self.s.vocab

@@ -92,6 +92,33 @@ def test_layer_ragged_sequences(gpu_lib, tokens):
     assert_same_fp32(host(xg), ref)
 
 
+@pytest.mark.parametrize("tokens", [3, 8])
+def test_layer_tinyllama_shape_few_tokens(gpu_lib, tokens):
+    """One layer at the TinyLLaMA-1.1B shape (hidden 2048, FFN 5632) with 3
+    and 8 tokens of one sequence at positions 100.. over a prefilled cache:
+    the fused-prologue GEMVs with several columns per pass, the down
+    projection's K = 5632 in three register chunks."""
+    qk = gpu_lib
+    g = W.Geometry(2048, 32, 4, 64, 5632)
+    cap, ctx = 160, 100
+    say(f"layer_forward TinyLLaMA shape tokens={tokens}")
+    wf = W.layer_weights_f32(43, 0, g)
+    wl = oracle_layer(wf)
+    lw = layer_to_device(wf)
+    kc, vc = W.kv_prefill_f16(43, 0, g.n_kv_heads, cap, g.head_dim, ctx)
+    kc, vc = kc.view(np.uint16).copy(), vc.view(np.uint16).copy()
+    kcg, vcg = dev(kc), dev(vc)
+    pos = (ctx + np.arange(tokens)).astype(np.int32)
+    seq = np.zeros(tokens, np.int32)
+    x = synth.normal(43, 5, (tokens, g.hidden))
+    ref = oracle.layer_forward(wl, g.cfg(cap), x, pos, seq, kc, vc)
+    xg = dev(x)
+    qk.layer_forward(lw, qk.layer_cfg(**g.cfg(cap)), xg, dev(pos), dev(seq), kcg, vcg)
+    assert rel_err(host(xg), ref) < LAYER_TOL
+    assert_same_fp32(host(xg), ref)
+    assert np.mean(host(kcg, np.uint16) == kc) > 0.999
+
+
 @pytest.mark.parametrize("seqs", [1, 3, 12])
 def test_layer_decode_through_ring_wrap(gpu_lib, seqs):
     """Decode past the cache capacity (the cache is a ring, position p in row
@@ -178,6 +205,56 @@ def check_routing(sel_g, w_g, sel_o, w_o, logits):
         assert srt[k - 1] - srt[k] < 1e-5, f"token {t}: selection differs without a near tie"
 
 
+def rowq_expert_ffn(x_row, gu_q, gu_r, dn_q, dn_r, bits):
+    """The oracle's expert FFN with row-scaled weights (the expert shape comes
+    from the arrays): Q8_0 input, gate/up, SwiGLU, Q8_0, down."""
+    F = gu_q.shape[0] // 2
+    xq, xd = oracle.quantize_q8_0(np.asarray(x_row, np.float32)[None])
+    gup = oracle.qmatmul_rowq(gu_q, gu_r, xq, xd, bits)[0]
+    hq, hd = oracle.quantize_q8_0(oracle.swiglu(gup[:F], gup[F:])[None])
+    return oracle.qmatmul_rowq(dn_q, dn_r, hq, hd, bits)[0]
+
+
+def selection_weights(logits, sel):
+    """The routing rule's weights for a given selection: s = sigmoid(logit)
+    in fp64 for each selected expert, w = s / (sum of s in rank order),
+    rounded to fp32."""
+    T, k = sel.shape
+    w = np.empty((T, k), np.float32)
+    for t in range(T):
+        s = 1.0 / (1.0 + np.exp(-logits[t, sel[t]].astype(np.float64)))
+        tot = 0.0
+        for r in range(k):
+            tot += s[r]
+        w[t] = (s / tot).astype(np.float32)
+    return w
+
+
+def combine(ys, w):
+    """sum over ranks, in rank order, of w[r] * ys[r], in fp64, rounded once."""
+    acc = np.zeros(len(ys[0]), np.float64)
+    for r in range(len(w)):
+        acc += np.float64(w[r]) * np.asarray(ys[r], np.float64)
+    return acc.astype(np.float32)
+
+
+def moe_expected(sel_g, w_g, sel_o, out_o, logits, expert_y):
+    """Expected output of every token.  Where the GPU chose the oracle's
+    experts it is the oracle's output.  Where a near tie gave another
+    selection (which check_routing accepted) it is the oracle's expert FFNs
+    under the GPU's selection, combined with the routing rule's weights for
+    that selection; the GPU's weights must equal those.  expert_y(t, e) is
+    the oracle's FFN of expert e on token t."""
+    want = np.array(out_o, np.float32, copy=True)
+    for t in range(sel_o.shape[0]):
+        if np.array_equal(sel_g[t], sel_o[t]):
+            continue
+        wt = selection_weights(logits[t:t + 1], sel_g[t:t + 1])[0]
+        assert np.allclose(w_g[t], wt, rtol=1e-6, atol=1e-8), f"token {t}: weights of the GPU's selection"
+        want[t] = combine([expert_y(t, int(e)) for e in sel_g[t]], wt)
+    return want
+
+
 @pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (1, 128, 8, 32, 1),
                                        # 1600 pairs: the grouping's second chunk of 1024,
                                        # about 100 tokens per expert (passes of 8 columns)
@@ -198,8 +275,10 @@ def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
     sel_g, w_g = host(sg), host(wg)
     check_routing(sel_g, w_g, sel, w, logits)
+    want = moe_expected(sel_g, w_g, sel, out, logits,
+                        lambda t, e: oracle.moe_expert_ffn(x[t], guq[e], gud[e], dnq[e], dnd[e]))
+    assert rel_err(host(y), want) < LAYER_TOL
     if np.array_equal(sel_g, sel):
-        assert rel_err(host(y), out) < LAYER_TOL
         assert_same_fp32(host(y), out)
     # every selection is a set of distinct experts and weights sum to 1
     assert all(len(set(r)) == k for r in sel_g)
@@ -225,8 +304,10 @@ def test_moe_rowq_matches_oracle(gpu_lib, bits, T, H, E, F, k):
                                                dev(dnr), bits)
     sel_g, w_g = host(sg), host(wg)
     check_routing(sel_g, w_g, sel, w, logits)
+    want = moe_expected(sel_g, w_g, sel, out, logits,
+                        lambda t, e: rowq_expert_ffn(x[t], guq[e], gur[e], dnq[e], dnr[e], bits))
+    assert rel_err(host(y), want) < LAYER_TOL
     if np.array_equal(sel_g, sel):
-        assert rel_err(host(y), out) < LAYER_TOL
         assert_same_fp32(host(y), out)
     assert all(len(set(r)) == k for r in sel_g)
 
