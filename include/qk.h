@@ -255,6 +255,22 @@ int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t 
 
 size_t qk_layer_workspace(const qk_layer_cfg* cfg, int64_t tokens);
 
+/* layer_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and errors as layer_forward, without the
+ * caller workspace.  The workspace is a device array of QK_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing.  A call whose qk_layer_workspace(cfg, tokens) exceeds
+ * QK_SCRATCH_BYTES returns QK_EWORKSPACE with nothing enqueued (the
+ * TinyLLaMA-1.1B shape fits for up to 8 tokens at cap 2176 and up to 3
+ * tokens at cap 8192).  Returns QK_EHIP when the array's device address
+ * cannot be obtained.  Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (different streams, not ordered) race. */
+#define QK_SCRATCH_BYTES (8u << 20)
+int qk_layer_forward_scratch(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t tokens,
+                             const int32_t* pos, const int32_t* seq, uint16_t* k_cache,
+                             uint16_t* v_cache, void* stream);
+
 /* First half of the feed-forward block [GUIDE 4.1, 4.4]:
  * h = SwiGLU(W_gate . Q8_0(u), W_up . Q8_0(u)), u = rmsnorm(x, gamma), with
  * W [2 ffn][hidden] Q4_0 (gate rows, then up rows).  x [tokens][hidden],

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqk.so")
 _lib = None
 
 QK_OK, QK_EINVAL, QK_ESHAPE, QK_EALIGN, QK_EWORKSPACE, QK_EHIP = 0, -1, -2, -3, -4, -5
+QK_SCRATCH_BYTES = 8 << 20   # device array behind qk_layer_forward_scratch (include/qk.h)
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -68,6 +69,8 @@ _SIGS = {
     "layer_forward": ([ctypes.POINTER(Layer), ctypes.POINTER(LayerCfg), _P, _I64, _P, _P, _P, _P,
                        _P, _SZ, _P], ctypes.c_int),
     "qk_layer_workspace": ([ctypes.POINTER(LayerCfg), _I64], _SZ),
+    "qk_layer_forward_scratch": ([ctypes.POINTER(Layer), ctypes.POINTER(LayerCfg), _P, _I64, _P, _P,
+                                  _P, _P, _P], ctypes.c_int),
     "moe_route_and_apply": ([_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
                              _SZ, _P], ctypes.c_int),
     "qk_moe_workspace": ([_I64, _I64, _I64, _I32, _I64], _SZ),
@@ -387,6 +390,19 @@ def layer_forward(w, cfg: LayerCfg, x, pos, seq, k_cache, v_cache, ws=None):
                                 _dev16(k_cache, "k_cache"),
                                 _dev16(v_cache, "v_cache"), wsb.data_ptr(), need,
                                 _stream()), "layer_forward")
+    return x
+
+
+def qk_layer_forward_scratch(w, cfg: LayerCfg, x, pos, seq, k_cache, v_cache):
+    """layer_forward without a caller workspace (the library's own device
+    array; calls that overlap on one GPU race).  x updated in place."""
+    t = x.shape[0]
+    st = w.struct() if isinstance(w, LayerWeights) else w
+    _check(load().qk_layer_forward_scratch(ctypes.byref(st), ctypes.byref(cfg),
+                                           _dev(x, torch.float32, "x"), t,
+                                           _dev(pos, torch.int32, "pos"), _dev(seq, torch.int32, "seq"),
+                                           _dev16(k_cache, "k_cache"), _dev16(v_cache, "v_cache"),
+                                           _stream()), "qk_layer_forward_scratch")
     return x
 
 

@@ -7,6 +7,7 @@
 // pattern with its own gain.  Every Q4_0 matmul reads Q8_0 activations
 // (llama.cpp guide 2.2); the FFN input is quantized once for gate and up.
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 
@@ -21,7 +22,7 @@ struct LayerWs {
     uint16_t* xd;     // [T][max/32]
     float* qkv;       // [T][Nqkv] (prefill path; the decode path keeps q only)
     float* h;         // [T][F]
-    void* att_ws;     // attention merge counters and chunk partials
+    void* att_ws;     // attention chunk records
     size_t att_bytes;
     size_t total;
 };
@@ -172,6 +173,54 @@ extern "C" int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* 
                      gemv_prologue_fits(c.ffn, tokens);
     if (few) return layer_decode(w, c, x, tokens, pos, seq, k_cache, v_cache, L, s);
     return layer_prefill(w, c, x, tokens, pos, seq, k_cache, v_cache, L, s);
+}
+
+// ------------------------------------------------ layer without a workspace
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the layer's workspace lives in a file-scope device array instead of
+// a caller buffer.  Each GPU holds its own copy of the array, whose device
+// address is looked up once per device (with that device current) on the
+// first call there; the kernels then receive that address like any
+// workspace.  Nothing in the workspace has to start at zero (every byte a
+// call reads was written earlier in the same call), and the array keeps the
+// last call's contents.  Calls that overlap on one GPU share the array and
+// race: they must be ordered (one stream, or synchronized streams).
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[QK_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];
+
+// Device address of this device's copy of `scratch` (null on failure).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int qk_layer_forward_scratch(const qk_layer* w, const qk_layer_cfg* cfg, float* x,
+                                        int64_t tokens, const int32_t* pos, const int32_t* seq,
+                                        uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+    int rc = check_cfg(cfg);
+    if (rc) return rc;
+    QK_REQUIRE(tokens >= 0 && tokens <= INT32_MAX, QK_EINVAL);
+    const size_t need = layer_layout(nullptr, *cfg, tokens).total;
+    QK_REQUIRE(need <= (size_t)QK_SCRATCH_BYTES, QK_EWORKSPACE);
+    if (tokens == 0) return QK_OK;
+    void* ws = scratch_for_current_device();
+    if (!ws) return QK_EHIP;
+    return layer_forward(w, cfg, x, tokens, pos, seq, k_cache, v_cache, ws, need, stream);
 }
 
 // ------------------------------------------------------------- FFN first half

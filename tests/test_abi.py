@@ -90,3 +90,9 @@ def test_workspace_queries_host_only(lib):
     assert lib.qk_lm_head_workspace(32000, 2048, 1) > 0
     assert lib.qk_gqa_attention_workspace(4, 32, 64, 2176) > 0
     assert lib.qk_moe_workspace(64, 6144, 256, 8, 2048) > 0
+
+
+def test_scratch_size_constant_matches_header():
+    """The binding's QK_SCRATCH_BYTES is the header's."""
+    m = re.search(r"#define QK_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == qk.QK_SCRATCH_BYTES
