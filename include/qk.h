@@ -271,6 +271,55 @@ int qk_layer_forward_scratch(const qk_layer* w, const qk_layer_cfg* cfg, float* 
                              const int32_t* pos, const int32_t* seq, uint16_t* k_cache,
                              uint16_t* v_cache, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Whole-model greedy decode in one persistent kernel                     */
+/* ---------------------------------------------------------------------- */
+
+/* A LLaMA-shaped decoder held on the device for qk_decode_greedy. */
+typedef struct qk_decoder {
+    const qk_layer* layers;    /* DEVICE array [n_layers] of layer weight pointers */
+    int64_t n_layers;
+    const float* embed;        /* [vocab][hidden] fp32 */
+    const float* gamma_final;  /* [hidden] */
+    const uint8_t* lm_q;       /* LM head Q4_0 [vocab][hidden] */
+    const uint16_t* lm_d;
+    int64_t vocab;
+    uint16_t* k_cache;         /* fp16 [n_layers][n_kv_heads][cap][head_dim], one sequence */
+    uint16_t* v_cache;
+} qk_decoder;
+
+/* n_tokens greedy decode steps of one sequence [GUIDE 2 pipeline figure:
+ * embedding, the decoder layers, final RMSNorm, LM head, argmax; each layer
+ * as layer_forward computes it for one token], all in one launch.
+ * Step j runs at position pos0 + j (ring row (pos0 + j) % cap of every
+ * layer's cache, attending to rows 0..min(pos0 + j, cap - 1)); its input
+ * token is forced[j] when `forced` is non-NULL (teacher forcing), else
+ * first_id[0] for j = 0 and the greedy token of step j - 1 after that.
+ * out_ids[j] (device, [n_tokens]) receives step j's greedy token (largest
+ * logit, lowest id on ties); when `logits` is non-NULL, step j's logits go
+ * to row j % logits_rows of logits [logits_rows][vocab].
+ * The kernel keeps one workgroup on every CU of the device, resident for the
+ * whole call, so no other work may run on the device meanwhile.  Its
+ * workgroups hand results to each other through `ws` (qk_decode_workspace
+ * bytes, 256-byte aligned; the call clears what it needs, so no
+ * initialization is required).  Every wait inside the kernel is bounded by
+ * spin_limit polls (0: 2^20, about a second): a wait that gives up ends the
+ * kernel early with wrong outputs and sets the flag that qk_decode_error
+ * reads.
+ * Shapes: head_dim 32 or 64; n_q_heads / n_kv_heads <= 8; hidden and
+ * n_q_heads * head_dim <= 2048; ffn <= 6144 (multiples of 32); cap at most
+ * 128 rows per attention chunk (8192 for the TinyLLaMA-1.1B shape on 256
+ * CUs); otherwise QK_ESHAPE.  Weight and gain pointers inside `layers` must
+ * be 16-byte aligned (they cannot be checked on the host). */
+size_t qk_decode_workspace(const qk_layer_cfg* cfg);
+int qk_decode_greedy(const qk_decoder* m, const qk_layer_cfg* cfg, const int32_t* first_id,
+                     const int32_t* forced, int64_t pos0, int64_t n_tokens, int32_t* out_ids,
+                     float* logits, int64_t logits_rows, uint32_t spin_limit, void* ws,
+                     size_t ws_bytes, void* stream);
+/* Synchronous: *flag (host) = nonzero when a wait of the last qk_decode_greedy
+ * on `ws` gave up.  Waits for the copy (not a call for the decode loop). */
+int qk_decode_error(const void* ws, const qk_layer_cfg* cfg, int32_t* flag);
+
 /* First half of the feed-forward block [GUIDE 4.1, 4.4]:
  * h = SwiGLU(W_gate . Q8_0(u), W_up . Q8_0(u)), u = rmsnorm(x, gamma), with
  * W [2 ffn][hidden] Q4_0 (gate rows, then up rows).  x [tokens][hidden],

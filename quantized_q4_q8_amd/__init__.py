@@ -46,6 +46,12 @@ class LayerCfg(ctypes.Structure):
                 ("ffn", _I64), ("eps", _F32), ("rope_base", _F32), ("cap", _I64)]
 
 
+class DecoderStruct(ctypes.Structure):
+    """qk_decoder of include/qk.h."""
+    _fields_ = [("layers", _P), ("n_layers", _I64), ("embed", _P), ("gamma_final", _P),
+                ("lm_q", _P), ("lm_d", _P), ("vocab", _I64), ("k_cache", _P), ("v_cache", _P)]
+
+
 _SIGS = {
     "qk_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "quantize_q8_0": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -82,6 +88,10 @@ _SIGS = {
     "qk_lm_head_workspace": ([_I64, _I64, _I64], _SZ),
     "qk_ffn_up": ([_P, _P, _F32, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
     "qk_ffn_up_workspace": ([_I64, _I64], _SZ),
+    "qk_decode_workspace": ([ctypes.POINTER(LayerCfg)], _SZ),
+    "qk_decode_greedy": ([ctypes.POINTER(DecoderStruct), ctypes.POINTER(LayerCfg), _P, _P, _I64, _I64,
+                          _P, _P, _I64, ctypes.c_uint32, _P, _SZ, _P], ctypes.c_int),
+    "qk_decode_error": ([_P, ctypes.POINTER(LayerCfg), _P], ctypes.c_int),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -483,3 +493,37 @@ def qk_moe_route_and_apply_rowq(x, w_router, top_k: int, gate_up_q, gate_up_r, d
         _dev(y, torch.float32, "y"), _dev(si, torch.int32, "sel_idx"), _dev(sw, torch.float32, "sel_w"),
         wsb.data_ptr(), need, _stream()), "qk_moe_route_and_apply_rowq")
     return y, si, sw
+
+
+# ---------------------------------------------------------------------------
+# whole-model greedy decode in one persistent kernel
+# ---------------------------------------------------------------------------
+def qk_decode_workspace(cfg: LayerCfg) -> int:
+    return int(load().qk_decode_workspace(ctypes.byref(cfg)))
+
+
+def qk_decode_greedy(dec: DecoderStruct, cfg: LayerCfg, n_tokens: int, pos0: int, out_ids,
+                     first_id=None, forced=None, logits=None, spin_limit: int = 0, ws=None):
+    """n_tokens greedy steps of one sequence from position pos0 (qk_decode_greedy
+    of include/qk.h).  out_ids [n_tokens] int32 receives the greedy tokens;
+    logits, when given, [rows][vocab] fp32 receives step j in row j % rows."""
+    need = qk_decode_workspace(cfg)
+    wsb = _ws(ws, need, out_ids.device)
+    rows = 0 if logits is None else logits.shape[0]
+    _check(load().qk_decode_greedy(ctypes.byref(dec), ctypes.byref(cfg),
+                                   None if first_id is None else _dev(first_id, torch.int32, "first_id"),
+                                   None if forced is None else _dev(forced, torch.int32, "forced"),
+                                   pos0, n_tokens, _dev(out_ids, torch.int32, "out_ids"),
+                                   None if logits is None else _dev(logits, torch.float32, "logits"),
+                                   rows, spin_limit, wsb.data_ptr(), need, _stream()),
+           "qk_decode_greedy")
+    return out_ids
+
+
+def qk_decode_error(cfg: LayerCfg, ws) -> int:
+    """The error flag of the last qk_decode_greedy on ws (synchronous)."""
+    buf = ws.buf if isinstance(ws, Workspace) else ws
+    flag = ctypes.c_int32(0)
+    _check(load().qk_decode_error(buf.data_ptr(), ctypes.byref(cfg), ctypes.byref(flag)),
+           "qk_decode_error")
+    return int(flag.value)

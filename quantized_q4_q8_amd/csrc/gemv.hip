@@ -20,54 +20,13 @@
 // once per block as -8 * sum(x).  The wave's row sums are reduced together
 // (row_sums) and the epilogue runs in the lanes that hold them.
 #include "internal.h"
+#include "qdot.h"
 
 #include <type_traits>
 
 namespace qk {
 
 namespace {
-
-__device__ __forceinline__ int dot_block(const uint4 w, const uint4 x0, const uint4 x1, int s) {
-    const uint32_t m4 = 0x0F0F0F0Fu;
-    s = __builtin_amdgcn_sdot4((int)(w.x & m4), (int)x0.x, s, false);
-    s = __builtin_amdgcn_sdot4((int)(w.y & m4), (int)x0.y, s, false);
-    s = __builtin_amdgcn_sdot4((int)(w.z & m4), (int)x0.z, s, false);
-    s = __builtin_amdgcn_sdot4((int)(w.w & m4), (int)x0.w, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.x >> 4) & m4), (int)x1.x, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.y >> 4) & m4), (int)x1.y, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.z >> 4) & m4), (int)x1.z, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.w >> 4) & m4), (int)x1.w, s, false);
-    return s;
-}
-
-__device__ __forceinline__ int byte_sum(const uint4 x0, const uint4 x1) {
-    const int ones = 0x01010101;
-    int s = 0;
-    s = __builtin_amdgcn_sdot4((int)x0.x, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x0.y, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x0.z, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x0.w, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x1.x, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x1.y, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x1.z, ones, s, false);
-    s = __builtin_amdgcn_sdot4((int)x1.w, ones, s, false);
-    return s;
-}
-
-// swish(g) * u of fp32 matmul outputs, in fp64, rounded once
-__device__ __forceinline__ float swiglu1(float g, float u) {
-    const double gd = (double)g;
-    return (float)(gd / (1.0 + exp(-gd)) * (double)u);
-}
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-// 16-byte weight load marked non-temporal: weights stream through once per
-// call and should not displace the activations from the caches.
-__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
-    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
@@ -172,58 +131,6 @@ __device__ __forceinline__ void stage_row(const RowRegs<KC>& R, int64_t k, float
             }
         }
     }
-}
-
-// Sums of N values per lane over the 64 lanes of a wave, all N at once.  Two
-// "transposed" butterfly steps across rows (lane offsets 32 and 16) halve
-// the value count each: a lane keeps the half its offset bit selects and adds
-// the partner's copy of it.  The remaining N / 4 values (at least one) are
-// then summed over the rest of the wave, ending with DPP steps inside each
-// 16-lane row, so every lane of a row holds the same complete sums.  Row
-// (b5, b4) of the wave (lane bits 5 and 4) holds value indices
-// b5 * N/2 + b4 * N/4 + k, k < max(N/4, 1) (for N < 4 the index is b5 when
-// N = 2, 0 when N = 1).  The order of additions is fixed, so the result is
-// deterministic.
-// The first value index whose sums row_sums leaves in the 16-lane row of
-// `lane` (see row_sums).
-template <int N>
-__device__ __forceinline__ int row_sums_base(int lane) {
-    int base = 0;
-    if (N >= 2 && (lane & 32) != 0) base += N / 2;
-    if (N >= 4 && (lane & 16) != 0) base += N / 4;
-    return base;
-}
-
-template <int N>
-__device__ __forceinline__ int row_sums(double (&v)[N], int lane) {
-    if (N >= 2) {
-        constexpr int h = N / 2;
-        const bool up = (lane & 32) != 0;
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-            const double send = up ? v[i] : v[i + h];
-            const double keep = up ? v[i + h] : v[i];
-            v[i] = keep + __shfl_xor(send, 32, WAVE);
-        }
-    }
-    if (N >= 4) {
-        constexpr int h = N / 4;
-        const bool up = (lane & 16) != 0;
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-            const double send = up ? v[i] : v[i + h];
-            const double keep = up ? v[i + h] : v[i];
-            v[i] = keep + __shfl_xor(send, 16, WAVE);
-        }
-    }
-    constexpr int NV = N >= 4 ? N / 4 : 1;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        if (N == 1) v[k] += __shfl_xor(v[k], 32, WAVE);
-        if (N <= 2) v[k] += __shfl_xor(v[k], 16, WAVE);
-        v[k] = group_sum<16>(v[k]);
-    }
-    return row_sums_base<N>(lane);
 }
 
 // Physical rows per output unit: SwiGLU units are (gate row, up row), QKV

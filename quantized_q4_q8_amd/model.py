@@ -13,8 +13,9 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (LayerWeights, Workspace, layer_cfg, layer_forward, qk_embed_lookup,
-               qk_layer_workspace, qk_lm_head, qk_lm_head_workspace, qk_quantize_q4_0)
+from . import (DecoderStruct, Layer, LayerWeights, Workspace, layer_cfg, layer_forward,
+               qk_decode_greedy, qk_decode_workspace, qk_embed_lookup, qk_layer_workspace,
+               qk_lm_head, qk_lm_head_workspace, qk_quantize_q4_0)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -101,6 +102,7 @@ class Decoder:
         self.lm_q, self.lm_d = next(it), next(it)
         self.structs = [lw.struct() for lw in self.layers]
         self.arena = arena
+        self._dstruct = None
 
     def reserve(self, tokens: int) -> None:
         """Size the workspace for calls of up to `tokens` tokens (before graph capture)."""
@@ -146,6 +148,28 @@ class Decoder:
                 self.step(ids[j:j + 1], positions[j], seq,
                           dict(x=x, logits=logits[r:r + 1], next=next_ids[j:j + 1]))
         return gr
+
+    def decoder_struct(self) -> DecoderStruct:
+        """The qk_decoder of this model for qk_decode_greedy (one sequence):
+        the layer table is copied to the device once."""
+        assert self.s.seqs == 1, "the persistent decode runs one sequence"
+        table = (Layer * len(self.structs))(*self.structs)
+        raw = bytes(table)
+        self.layer_table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        self.decode_ws = Workspace()
+        self.decode_ws.reserve(qk_decode_workspace(self.cfg), self.device)
+        return DecoderStruct(self.layer_table.data_ptr(), len(self.structs), self.embed.data_ptr(),
+                             self.gamma_final.data_ptr(), self.lm_q.data_ptr(), self.lm_d.data_ptr(),
+                             self.s.vocab, self.k_cache.data_ptr(), self.v_cache.data_ptr())
+
+    def decode_persistent(self, n: int, pos0: int, out_ids: torch.Tensor, first_id=None, forced=None,
+                          logits=None, spin_limit: int = 0) -> torch.Tensor:
+        """n greedy steps from position pos0 in one persistent kernel launch."""
+        if getattr(self, "_dstruct", None) is None:
+            self._dstruct = self.decoder_struct()
+        return qk_decode_greedy(self._dstruct, self.cfg, n, pos0, out_ids, first_id=first_id,
+                                forced=forced, logits=logits, spin_limit=spin_limit,
+                                ws=self.decode_ws)
 
     def step_buffers(self, tokens: int) -> dict:
         """Preallocated buffers so that `step` allocates nothing (graph capture)."""
