@@ -52,8 +52,10 @@ constexpr int MAXHD = 64;
 constexpr int CH_ROWS = 64;           // cache rows per attention pass (one per lane)
 constexpr int CH_PASSES = 2;          // passes per chunk: at most 128 rows
 constexpr int MAXCPH = 64;            // attention chunks per KV head
-constexpr int LM_UPW = 8;             // LM-head rows per compute wave and pass
+constexpr int LM_UPW = 4;             // LM-head rows per compute wave and pass
 constexpr int MAXDS = 8;              // head dims per merge workgroup
+constexpr int MAXWG = 512;            // workgroups (one per CU)
+constexpr int MAXL = 64;              // layers
 // 16-byte pieces of the chunk's K rows (and as many of its V rows) per
 // compute thread
 constexpr int KVH = (CH_PASSES * CH_ROWS * (MAXHD / 8) + CWT - 1) / CWT;
@@ -61,9 +63,11 @@ constexpr int KVH = (CH_PASSES * CH_ROWS * (MAXHD / 8) + CWT - 1) / CWT;
 #if defined(__HIP_DEVICE_COMPILE__)
 #define GLB __attribute__((address_space(1)))
 #define CONSTAS __attribute__((address_space(4)))
+#define LDSAS __attribute__((address_space(3)))
 #else
 #define GLB
 #define CONSTAS
+#define LDSAS
 #endif
 
 struct DecodeArgs {
@@ -86,7 +90,8 @@ struct DecodeArgs {
     //  oor [nq][cph][hd][2] chunk outputs, fp64 as two words
     //  oo  [nq * hd] attention output;  oh [F] SwiGLU output
     //  olm [nwg][2] each workgroup's best logit and its row
-    //  olf [nwg][2] each workgroup's completion flag of the latest phase
+    //  olf [MAXWG][2] each workgroup's completion flag of the latest phase
+    //      (a 32-bit tag at the head of a 16-byte slot)
     uint64_t* xw;
     int32_t ox, ox1, oq, okv, oml, oor, oo, oh, olm, olf;
     int32_t* ctl;                 // [0]: error flag
@@ -97,10 +102,14 @@ struct DecodeArgs {
     double theta[MAXHD / 2];      // RoPE base^(-2i/hd), fp64 from the host
 };
 
-// The kernel's arguments and the layer table are read through the constant
-// address space: scalar loads, and no private copy of the argument struct.
-typedef const CONSTAS DecodeArgs KArgs;
-typedef const CONSTAS qk_layer KLayer;
+// The kernel copies its arguments and the layer table into LDS once and reads
+// them there.  Read from the argument segment or global memory instead, a
+// read that the compiler places under divergent control flow becomes a
+// vector load, and waiting for it (loads complete in order) would wait for
+// every weight prefetch in flight.
+typedef const LDSAS DecodeArgs KArgs;
+typedef const LDSAS qk_layer KLayer;
+typedef const CONSTAS DecodeArgs CArgs;
 
 // ------------------------------------------------------------ memory access
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
@@ -305,9 +314,20 @@ struct Lds {
     int lm_i[CWV];
     int lm_cnt;
     int arrive;                     // compute waves done with the current phase
-    uint32_t ready;                 // tag whose completion flags the gathering wave 0 has seen
+    uint32_t ready;                 // tag whose completion flags the gathering waves have seen
+    uint32_t flagged;               // tag of this workgroup's latest completion flag
     int fail;
+    DecodeArgs args;                // the kernel's arguments
+    qk_layer layers[MAXL];          // the layer table
 };
+
+// Layer l's entry of the table, addressed from the (per-phase laundered)
+// argument pointer so that the compiler cannot hoist the reads and keep them
+// live across phases.
+__device__ __forceinline__ KLayer& layer_of(KArgs* pa, int l) {
+    const LDSAS char* base = (const LDSAS char*)pa + (offsetof(Lds, layers) - offsetof(Lds, args));
+    return ((KLayer*)base)[l];
+}
 
 // RMSNorm (optional) and Q8_0 of K staged values into lxq / lxd, by every
 // thread: groups of 4 values, 8 threads per 32-block, with the arithmetic of
@@ -392,35 +412,51 @@ struct IoWave {
         if (!ok && lane == 0) S.fail = 1;
     }
 
-    // Waits until every workgroup has flagged the phase `tag` done: wave 0
-    // polls the flags (small: one pair per workgroup) and posts the tag in
-    // LDS, the other gathering waves wait for that post.  Only then are the
-    // phase's outputs read, once: polling the outputs themselves from every
-    // workgroup at once would flood the memory side.  (A flag can be seen
-    // before some of its workgroup's outputs; their tags catch that.)
+    // Waits until every workgroup has flagged the phase `tag` done.  Each
+    // workgroup's flag is a 32-bit word at the head of its own 16-byte slot
+    // (eight workgroups share a 128-byte line: packing them tighter makes
+    // the writers and the pollers of a line contend).  Gathering waves 0 and
+    // 1 poll, all of a lane's loads in flight at once and wave 1's polls
+    // half a round trip behind wave 0's, so that the last flag is seen soon
+    // after it lands; the first of them to see every flag posts the tag in
+    // LDS, where the other gathering waves wait.  Only then are the phase's
+    // outputs read, once: polling the outputs themselves from every
+    // workgroup would flood the memory side.  A flag can be seen before some
+    // of its workgroup's outputs, whose tags catch that; a workgroup may
+    // already have flagged a later phase (flags only grow within a launch),
+    // hence "at least".
     __device__ __forceinline__ bool wait_flags(uint32_t tag) {
         KArgs& a = *pa;
-        if (io == 0) {
-            const __amdgpu_buffer_rsrc_t rw = rsrc(uni(a.xw));
+        if (io < 2) {
+            const __amdgpu_buffer_rsrc_t rf = rsrc(uni(a.xw + a.olf));
             const int nwg = (int)gridDim.x;
-            // A workgroup may already have flagged a later phase (flags only
-            // grow within a launch), hence "at least", not "equal".
-            for (int base = 0; base < nwg; base += WAVE) {
-                const int w = base + lane;
-                const uint32_t off = (uint32_t)(a.olf / 2 + (w < nwg ? w : 0)) * 16u;
-                uint4 v = ld16(rw, off, CP_SC1);
-                uint32_t spins = 0;
-                while (__any(v.y < tag || v.w < tag)) {
-                    if (++spins > a.spin_limit) return false;
-                    if ((spins & 15) == 0 && ctl_error(a)) return false;
-                    v = ld16(rw, off, CP_SC1);
-                }
+            if (io == 1) {
+                __builtin_amdgcn_s_sleep(8);
+                __builtin_amdgcn_s_sleep(8);
             }
-            if (lane == 0) __hip_atomic_store(&S.ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            uint32_t v[MAXWG / WAVE];
+#pragma unroll
+            for (int k = 0; k < MAXWG / WAVE; ++k)
+                if (k * WAVE < nwg) v[k] = ld16(rf, (uint32_t)(k * WAVE + lane) * 16u, CP_SC1).x;
+            uint32_t spins = 0;
+            for (;;) {
+                bool stale = false;
+#pragma unroll
+                for (int k = 0; k < MAXWG / WAVE; ++k) stale |= k * WAVE + lane < nwg && v[k] < tag;
+                if (!__any(stale)) break;
+                if (__hip_atomic_load(&S.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= tag) return true;
+                if (++spins > a.spin_limit) return false;
+                if ((spins & 15) == 0 && ctl_error(a)) return false;
+#pragma unroll
+                for (int k = 0; k < MAXWG / WAVE; ++k)
+                    if (k * WAVE < nwg && __any(k * WAVE + lane < nwg && v[k] < tag))
+                        v[k] = ld16(rf, (uint32_t)(k * WAVE + lane) * 16u, CP_SC1).x;
+            }
+            if (lane == 0) __hip_atomic_fetch_max(&S.ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return true;
         }
         uint32_t spins = 0;
-        while (__hip_atomic_load(&S.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != tag) {
+        while (__hip_atomic_load(&S.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < tag) {
             if (__hip_atomic_load(&S.fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
             if (++spins > a.spin_limit) return false;
             __builtin_amdgcn_s_sleep(1);
@@ -500,7 +536,7 @@ struct IoWave {
     // fetched by wave 0) and gamma_attn
     __device__ __forceinline__ void A(int j, int l, uint32_t tbase) {
         KArgs& a = *pa;
-        KLayer& lw = ((KLayer*)a.layers)[l];
+        KLayer& lw = layer_of(pa, l);
         const int H = a.H;
         gamma(lw.gamma_attn, H);
         if (l > 0) {
@@ -668,7 +704,7 @@ struct IoWave {
                 stage_q8(S, S.u2.rawT, pa->nq * pa->hd, false, 0.0f);
                 lds_sync();
                 launder();
-                gamma(((KLayer*)pa->layers)[l].gamma_ffn, pa->H);          // E
+                gamma(layer_of(pa, l).gamma_ffn, pa->H);                    // E
                 fail(wait_flags(tA + 3) && vec<MAXH / 2 / IOP>(S.rawE, pa->ox1, pa->H, tA + 3, true));
                 lds_sync();
                 if (S.fail) return;
@@ -729,23 +765,23 @@ struct Compute {
 
     __device__ __forceinline__ void issue_qkv(int l) {
         KArgs& a = *pa;
-        KLayer& w = ((KLayer*)a.layers)[l];
+        KLayer& w = layer_of(pa, l);
         issue<1, 2, 1, KIND_QKV>(s0, w.w_qkv_q, w.w_qkv_d, a.H / QBLK,
                                  (a.nq + 2 * a.nkv) * a.hd / 2, 0, gw, nwc, lane);
     }
     __device__ __forceinline__ void issue_o(int l) {
         KArgs& a = *pa;
-        KLayer& w = ((KLayer*)a.layers)[l];
+        KLayer& w = layer_of(pa, l);
         issue<1, 1, 1, KIND_PLAIN>(s1, w.w_o_q, w.w_o_d, a.nq * a.hd / QBLK, a.H, 0, gw, nwc, lane);
     }
     __device__ __forceinline__ void issue_gu(int l) {
         KArgs& a = *pa;
-        KLayer& w = ((KLayer*)a.layers)[l];
+        KLayer& w = layer_of(pa, l);
         issue<2, 2, 1, KIND_SWIGLU>(s0, w.w_gate_up_q, w.w_gate_up_d, a.H / QBLK, a.F, a.F, gw, nwc, lane);
     }
     __device__ __forceinline__ void issue_dn(int l) {
         KArgs& a = *pa;
-        KLayer& w = ((KLayer*)a.layers)[l];
+        KLayer& w = layer_of(pa, l);
         issue<1, 1, 3, KIND_PLAIN>(s1, w.w_down_q, w.w_down_d, a.F / QBLK, a.H, 0, gw, nwc, lane);
     }
     __device__ __forceinline__ void issue_lm(int pass) {
@@ -810,16 +846,27 @@ struct Compute {
     }
 
     // This wave is done with phase `tag`; the last of the workgroup's compute
-    // waves to get here raises the workgroup's completion flag.
+    // waves to get here raises the workgroup's completion flag, and every
+    // compute wave waits for that before it goes on to issue the next weight
+    // prefetch.  A CU's memory requests leave in issue order, so outputs or a
+    // flag issued behind another wave's prefetch (tens of KB per CU) would
+    // wait for it, and so would every workgroup that polls them.
     __device__ __forceinline__ void arrive(uint32_t tag) {
         KArgs& a = *pa;
         if (lane == 0) {
             if (atomicAdd(&S.arrive, 1) == CWV - 1) {
                 S.arrive = 0;
-                put(a.xw + a.olf + 2 * wg, 0u, tag);
-                put(a.xw + a.olf + 2 * wg + 1, 0u, tag);
+                __hip_atomic_store((GLB uint32_t*)(a.xw + a.olf + 2 * wg), tag, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&S.flagged, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
+        // (the last arriver is a wave of this workgroup that waits on nothing
+        // global before it gets here; the bound is a guard)
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&S.flagged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < tag &&
+               ++spins <= a.spin_limit)
+            __builtin_amdgcn_s_sleep(1);
     }
 
     // A: QKV rows, RoPE, q out, K/V to the cache and the exchange
@@ -1039,6 +1086,7 @@ struct Compute {
                 stage_q8(S, S.rawA, pa->H, true, pa->eps);
                 lds_sync();
                 A(l, pa->pos0 + j, tA);
+                arrive(tA);
                 issue_gu(l);
                 kv_to_lds(pa->pos0 + j);
                 lds_sync();                                   // B
@@ -1102,9 +1150,19 @@ struct Compute {
 // The whole decode.  Grid: one workgroup per CU (all resident).
 __global__ __launch_bounds__(DT) void k_decode(const DecodeArgs args) {
     (void)args;   // read through the kernel-argument segment below
-    KArgs* kp = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    const CArgs* kp = (const CArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     __shared__ Lds S;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    static_assert(sizeof(DecodeArgs) % 4 == 0 && sizeof(qk_layer) % 4 == 0, "word copies");
+    for (int i = tid; i < (int)(sizeof(DecodeArgs) / 4); i += DT)
+        reinterpret_cast<uint32_t*>(&S.args)[i] = reinterpret_cast<const CONSTAS uint32_t*>(kp)[i];
+    {
+        const GLB uint32_t* src = (const GLB uint32_t*)kp->layers;
+        const int nw = kp->L * (int)(sizeof(qk_layer) / 4);
+        for (int i = tid; i < nw; i += DT) reinterpret_cast<uint32_t*>(&S.layers[0])[i] = src[i];
+    }
+    __syncthreads();
+    KArgs* pa = (KArgs*)&S.args;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int wg = blockIdx.x, nwg = (int)gridDim.x;
     if (tid == 0) {
@@ -1112,16 +1170,17 @@ __global__ __launch_bounds__(DT) void k_decode(const DecodeArgs args) {
         S.lm_cnt = 0;
         S.arrive = 0;
         S.ready = 0;
+        S.flagged = 0;
     }
     if (wave >= CWV) {
-        IoWave io{kp, S, wave - CWV, lane, wg};
+        IoWave io{pa, S, wave - CWV, lane, wg};
         io.run();
     } else {
-        Compute c{kp, S, tid, lane, wave, wg, wave * nwg + wg, CWV * nwg};
+        Compute c{pa, S, tid, lane, wave, wg, wave * nwg + wg, CWV * nwg};
         c.run();
     }
     // a workgroup that stopped on an error records it for every workgroup
-    if (tid == 0 && S.fail) set_error(*kp);
+    if (tid == 0 && S.fail) set_error(*pa);
 }
 
 // Clears the exchange words and the error flag before a decode.
@@ -1169,7 +1228,7 @@ DecodeLayout decode_layout(const qk_layer_cfg& c, int nwg) {
     d.o = take(Nq);
     d.h = take(c.ffn);
     d.lm = take(2 * (size_t)nwg);
-    d.lf = take(2 * (size_t)nwg);
+    d.lf = take(2 * (size_t)MAXWG);
     d.ctl = take(8);
     d.total_words = o;
     d.bytes = al256(o * 8);
@@ -1182,6 +1241,7 @@ int decode_shape_ok(const qk_layer_cfg& c, int nwg, int64_t vocab) {
     const int64_t H = c.hidden, Nq = c.n_q_heads * c.head_dim, F = c.ffn;
     const int64_t Nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
     if (nwg <= 0) return QK_EHIP;
+    if (nwg > MAXWG) return QK_ESHAPE;
     if (c.head_dim != 32 && c.head_dim != 64) return QK_ESHAPE;
     if (c.n_q_heads % c.n_kv_heads || c.n_q_heads / c.n_kv_heads > MAXG) return QK_ESHAPE;
     if (H > MAXH || Nq > MAXH || F > MAXF || H % QBLK || F % QBLK || Nq % QBLK) return QK_ESHAPE;
@@ -1219,7 +1279,8 @@ extern "C" int qk_decode_greedy(const qk_decoder* m, const qk_layer_cfg* cfg,
     QK_REQUIRE(cfg->hidden > 0 && cfg->n_q_heads > 0 && cfg->n_kv_heads > 0 && cfg->head_dim > 0 &&
                    cfg->ffn > 0 && cfg->cap > 0,
                QK_EINVAL);
-    QK_REQUIRE(m->n_layers > 0 && m->n_layers <= 4096 && m->vocab > 0, QK_EINVAL);
+    QK_REQUIRE(m->n_layers > 0 && m->vocab > 0, QK_EINVAL);
+    if (m->n_layers > MAXL) return QK_ESHAPE;
     QK_REQUIRE(n_tokens >= 0 && pos0 >= 0 && pos0 + n_tokens <= INT32_MAX, QK_EINVAL);
     QK_REQUIRE((uint64_t)n_tokens * (uint64_t)(6 * m->n_layers + 1) < (1ull << 31), QK_EINVAL);
     if (n_tokens == 0) return QK_OK;
