@@ -62,10 +62,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "longctx", "matmul", "prefill", "moe", "sample"],
+                    choices=["decode", "longctx", "longctx32k", "matmul", "prefill", "moe", "sample"],
                     help="decode (the headline line); the others measure decode past an "
-                         "8192-row ring cache and the standalone matmul, prefill, MoE and "
-                         "sampler workloads")
+                         "8192-row or a 32768-row ring cache and the standalone matmul, "
+                         "prefill, MoE and sampler workloads")
     ap.add_argument("--codec", default="q4_0", choices=["q4_0", "int4row", "int2row"],
                     help="weight format of the matmul and moe workloads: Q4_0 (fp16 scale per "
                          "32-block) or row-scaled int4 / int2 (fp32 scale per row)")
@@ -174,7 +174,9 @@ def decode_bytes_per_token(spec) -> float:
     return lin * q4 + kv + norms + H * 4
 
 
-def run_decode(args, long_context: bool = False):
+def run_decode(args, long_context=False):
+    """long_context: False (the headline workload), True (8192-row ring) or
+    "32k" (32768-row ring)."""
     import numpy as np
     import torch
 
@@ -182,7 +184,7 @@ def run_decode(args, long_context: bool = False):
     from synth import normal
     from synth import workloads as W
 
-    spec = W.DECODE_LONG if long_context else W.DECODE
+    spec = (W.DECODE_LONG32K if long_context == "32k" else W.DECODE_LONG) if long_context else W.DECODE
     g, L = spec["geometry"], spec["layers"]
     steps_per_run = max(1, min(args.decode_tokens, spec["steps"]))
     want_cpu = not args.no_cpu_baseline
@@ -287,7 +289,7 @@ def run_decode(args, long_context: bool = False):
     step_bytes = decode_bytes_per_token(spec)
     c0, c1 = spec["context"], spec["context"] + steps_per_run - 1
     if long_context:
-        metric = "decode tokens/s at TinyLLaMA-1.1B Q4_0 shape, 8192-row ring KV cache"
+        metric = f"decode tokens/s at TinyLLaMA-1.1B Q4_0 shape, {spec['cap']}-row ring KV cache"
         workload = (f"tinyllama-1.1b-shape greedy decode, 22 layers, positions {c0}->{c1} "
                     f"through an {spec['cap']}-row ring cache (every step attends {spec['cap']} positions)")
     else:
@@ -728,7 +730,8 @@ def main():
         sys.exit(1)
     import quantized_q4_q8_amd as qk
     qk.load()
-    {"decode": run_decode, "longctx": lambda a: run_decode(a, long_context=True), "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
+    {"decode": run_decode, "longctx": lambda a: run_decode(a, long_context=True),
+     "longctx32k": lambda a: run_decode(a, long_context="32k"), "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
 
 
 if __name__ == "__main__":

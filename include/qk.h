@@ -195,8 +195,8 @@ int qk_sample(const float* logits, int64_t rows, int64_t vocab, int32_t top_k, f
  * s_j = q . k_j / sqrt(head_dim), p = softmax(s), out = sum_j p_j v_j.
  * q, out [tokens][n_q_heads][head_dim] fp32; caches fp16
  * [seqs][n_kv_heads][cap][head_dim]; pos, seq int32 [tokens] (device,
- * pos >= 0; a negative position gives zeros).  head_dim must be 32 or 64 and
- * n_q_heads / n_kv_heads at most 512 / head_dim.  ws:
+ * pos >= 0; a negative position gives zeros).  head_dim must be 32 or 64,
+ * n_q_heads / n_kv_heads at most 512 / head_dim and cap at most 32768.  ws:
  * qk_gqa_attention_workspace() bytes. */
 int gqa_attention(const float* q, int64_t tokens, int64_t n_q_heads, int64_t n_kv_heads,
                   int64_t head_dim, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -247,7 +247,7 @@ typedef struct qk_layer_cfg {
  * p % cap.  A sequence with more than one token in the call must keep its
  * positions below cap (its later rows would overwrite positions its earlier
  * tokens attend to); a sequence with one token may be at any position.
- * cap <= 8192.
+ * cap <= 32768.
  * ws: qk_layer_workspace(cfg, tokens) bytes. */
 int layer_forward(const qk_layer* w, const qk_layer_cfg* cfg, float* x, int64_t tokens,
                   const int32_t* pos, const int32_t* seq, uint16_t* k_cache, uint16_t* v_cache,

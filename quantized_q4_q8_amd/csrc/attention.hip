@@ -7,9 +7,13 @@
 // Few tokens (decode): split over the context in two passes.  The chunk
 // pass reads each 64-row chunk of a KV head once for all query heads of its
 // group and writes one record per (head, chunk); the merge pass combines a
-// head's records by log-sum-exp rescaling.  The kernel boundary between them
-// is the cheapest way to make the records of every die visible to the
-// merging workgroup.  Many tokens (prefill): one pass over the chunks with
+// head's records by log-sum-exp rescaling, up to 512 chunks per head (cap up
+// to 32768 rows).  The kernel boundary between them is the cheapest way
+// measured to make the records of every die visible to the merging
+// workgroup: merging inside the chunk pass (the last workgroup of a KV head
+// to finish, found with a device-scope counter, merges its heads) was slower
+// on the TinyLLaMA-shape decode, its record stores, counter and record loads
+// being three dependent device-scope round trips.  Many tokens (prefill): one pass over the chunks with
 // an online softmax, its two products on the fp64 matrix cores.
 // Scores, softmax and the weighted sums are fp64 and the output is rounded
 // once to fp32.
@@ -20,7 +24,7 @@ namespace qk {
 namespace {
 
 constexpr int ACH = 64;            // cache rows per chunk: one per lane
-constexpr int MAX_CHUNKS = 128;    // chunks per head (cap <= 8192)
+constexpr int MAX_CHUNKS = 512;    // chunks per head (cap <= 32768)
 constexpr int64_t FLASH_MIN_TOKENS = 8;   // more tokens than this: the tiled pass
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -162,11 +166,13 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
 // Merge pass: workgroup (head h, token t) combines the head's chunk records
 // by log-sum-exp rescaling, out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Thread (pair i, slice s) owns output dimensions 2i, 2i + 1 over chunks
-// s, s + SLICES, ...; thread c also loads chunk c's (m, l).  Every load is
-// issued before anything waits; the chunk weights are then formed one per
-// thread.  Slice sums are added in slice order, so the result does not
-// depend on timing.  Writes the fp32 output and/or its Q8_0 codes (four
-// lanes per block).
+// s, s + SLICES, ...; threads c and c + 256 load chunk c's and chunk
+// c + 256's (m, l).  The (m, l) loads and a thread's first PB output pairs
+// are issued before anything waits; the chunk weights are then formed one
+// per chunk, and longer contexts load their further pairs PB at a time.  A
+// thread adds its chunks in order and the slice sums are added in slice
+// order, so the result does not depend on timing.  Writes the fp32 output
+// and/or its Q8_0 codes (four lanes per block).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ rec, int64_t nq,
                                                     int64_t nch, int64_t cap,
@@ -176,7 +182,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
                                                     uint16_t* __restrict__ od) {
     constexpr int PAIRS = HD / 2;
     constexpr int SLICES = 256 / PAIRS;
-    constexpr int PER = (MAX_CHUNKS + SLICES - 1) / SLICES;
+    constexpr int PB = 16;   // output pairs per thread per round of loads
+    static_assert(MAX_CHUNKS == 512, "(m, l) of two chunks per thread");
     __shared__ double wsh[MAX_CHUNKS];
     __shared__ double red[4];
     __shared__ double2 acc_s[SLICES][PAIRS];
@@ -190,32 +197,41 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
     const int pr = tid % PAIRS, sl = tid / PAIRS;
 
-    // all loads first: chunk tid's (m, l) and this thread's output pairs
-    const double2 ml = tid < used ? *reinterpret_cast<const double2*>(hr + tid * (HD + 2))
-                                  : make_double2(-INFINITY, 0.0);
-    double2 xv[PER];
+    const double2 ml0 = tid < used ? *reinterpret_cast<const double2*>(hr + tid * (HD + 2))
+                                   : make_double2(-INFINITY, 0.0);
+    const double2 ml1 = tid + 256 < used ? *reinterpret_cast<const double2*>(hr + (tid + 256) * (HD + 2))
+                                         : make_double2(-INFINITY, 0.0);
+    double2 xv[PB];
+    auto load_pairs = [&](int e0) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int cc = sl + e * SLICES;
-        xv[e] = cc < used ? *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr)
-                          : make_double2(0.0, 0.0);
-    }
-    double mx = group_max<WAVE>(ml.x);
+        for (int e = 0; e < PB; ++e) {
+            const int cc = sl + (e0 + e) * SLICES;
+            xv[e] = cc < used ? *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr)
+                              : make_double2(0.0, 0.0);
+        }
+    };
+    load_pairs(0);
+    double mx = group_max<WAVE>(fmax(ml0.x, ml1.x));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
     mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    const double wc = tid < used ? exp(ml.x - mx) : 0.0;
-    if (tid < MAX_CHUNKS) wsh[tid] = wc;
-    const double ls = group_sum<WAVE>(wc * ml.y);
+    const double wc0 = tid < used ? exp(ml0.x - mx) : 0.0;
+    const double wc1 = tid + 256 < used ? exp(ml1.x - mx) : 0.0;
+    wsh[tid] = wc0;
+    wsh[tid + 256] = wc1;
+    const double ls = group_sum<WAVE>(wc0 * ml0.y + wc1 * ml1.y);
     __syncthreads();   // everyone has read red[]; wsh is complete
     if (lane == 0) red[wave] = ls;
     double a0 = 0.0, a1 = 0.0;
+    for (int e0 = 0; sl + e0 * SLICES < used; e0 += PB) {
+        if (e0 > 0) load_pairs(e0);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int cc = sl + e * SLICES;
-        if (cc < used) {
-            a0 = fma(wsh[cc], xv[e].x, a0);
-            a1 = fma(wsh[cc], xv[e].y, a1);
+        for (int e = 0; e < PB; ++e) {
+            const int cc = sl + (e0 + e) * SLICES;
+            if (cc < used) {
+                a0 = fma(wsh[cc], xv[e].x, a0);
+                a1 = fma(wsh[cc], xv[e].y, a1);
+            }
         }
     }
     acc_s[sl][pr] = make_double2(a0, a1);

@@ -57,7 +57,7 @@ int check_cfg(const qk_layer_cfg* c) {
     if (c->n_q_heads % c->n_kv_heads) return QK_ESHAPE;
     if (c->head_dim != 32 && c->head_dim != 64) return QK_ESHAPE;
     if ((c->n_q_heads / c->n_kv_heads) * c->head_dim > 512) return QK_ESHAPE;
-    if (c->cap > 8192) return QK_ESHAPE;   // chunk-merge limit of the attention kernel
+    if (c->cap > 32768) return QK_ESHAPE;   // chunk-merge limit of the attention kernels
     return QK_OK;
 }
 

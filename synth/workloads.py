@@ -134,6 +134,9 @@ DECODE = dict(seed=2, geometry=TINYLLAMA, layers=22, vocab=32000, context=2048, 
 # brim; positions 8192..8319 wrap, so every step attends to 8192 positions.
 DECODE_LONG = dict(seed=5, geometry=TINYLLAMA, layers=22, vocab=32000, context=8192, steps=128,
                    cap=8192)
+# The same at a 32768-row ring (512 attention chunks per KV head).
+DECODE_LONG32K = dict(seed=6, geometry=TINYLLAMA, layers=22, vocab=32000, context=32768, steps=128,
+                      cap=32768)
 # C4: TinyLLaMA-1.1B-shaped prefill: batch 4 x 512 uniform token ids, causal, full logits.
 PREFILL = dict(seed=3, geometry=TINYLLAMA, layers=22, vocab=32000, batch=4, prompt=512, cap=512)
 # C5: MoE layer, hidden 6144, 256 experts of width 2048, sigmoid top-8, 64 tokens.

@@ -161,6 +161,44 @@ def test_layer_decode_through_ring_wrap(gpu_lib, seqs):
     assert np.mean(host(kcg, np.uint16) == kc) > 0.999
 
 
+@pytest.mark.parametrize("cap,tokens,start", [(32768, 2, 32768 + 5),   # one token per sequence, ring wrapped
+                                              (16384, 40, 9000)])      # a 40-token run past 8192: tiled path
+def test_layer_long_context(gpu_lib, cap, tokens, start):
+    """TinyLLaMA attention heads (32 query, 4 KV, head_dim 64) over long fp16
+    caches filled with N(0,1) rows: decode of one token per sequence at a
+    wrapped position of a 32768-row ring (512 attention chunks per head,
+    merged in the merge pass), and a 40-token prefill run at positions
+    9000..9039 of a 16384-row cache (the matrix-core attention pass)."""
+    qk = gpu_lib
+    g = W.Geometry(512, 32, 4, 64, 704)
+    one_each = tokens <= 8
+    seqs = tokens if one_each else 1
+    say(f"layer_forward long context cap={cap} tokens={tokens} start={start}")
+    wf = W.layer_weights_f32(43, 1, g)
+    wl = oracle_layer(wf)
+    lw = layer_to_device(wf)
+    kc, vc = W.kv_prefill_f16(43, 1, g.n_kv_heads, cap, g.head_dim, cap, seqs=seqs)
+    kc, vc = kc.view(np.uint16).copy(), vc.view(np.uint16).copy()
+    kcg, vcg = dev(kc), dev(vc)
+    x = synth.normal(43, 7, (tokens, g.hidden))
+    if one_each:
+        pos = np.full(tokens, start, np.int32) + np.arange(tokens, dtype=np.int32) * 977
+        seq = np.arange(tokens, dtype=np.int32)
+    else:
+        pos = (start + np.arange(tokens)).astype(np.int32)
+        seq = np.zeros(tokens, np.int32)
+    ref = oracle.layer_forward(wl, g.cfg(cap), x, pos, seq, kc, vc)
+    xg = dev(x)
+    qk.layer_forward(lw, qk.layer_cfg(**g.cfg(cap)), xg, dev(pos), dev(seq), kcg, vcg)
+    assert rel_err(host(xg), ref) < LAYER_TOL
+    assert_same_fp32(host(xg), ref)
+    # the rows written at the tokens' positions
+    got_k = oracle.f16_to_f32(host(kcg, np.uint16))
+    rows = pos % cap
+    for t in range(tokens):
+        assert rel_err(got_k[seq[t], :, rows[t]], oracle.f16_to_f32(kc[seq[t], :, rows[t]])) < LAYER_TOL
+
+
 def test_layer_decode_equals_prefill_last_row(gpu_lib):
     qk = gpu_lib
     g = W.LAYER_SMALL["geometry"]

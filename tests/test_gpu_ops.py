@@ -323,6 +323,10 @@ ATT_CASES = [
     (2, 32, 4, 64, 8192, 2, "ring"),
     (3, 8, 2, 64, 100, 3, "ring"),
     (12, 16, 2, 64, 100, 12, "ring"),     # many tokens: the tiled pass
+    # long contexts: up to 512 chunks per head in the merge pass
+    (2, 32, 4, 64, 32768, 2, "ring"),
+    (2, 16, 2, 32, 32768, 2, "ring"),
+    (40, 32, 4, 64, 16384, 1, "long9k"),  # many tokens past 8192: the tiled pass
     # head groups that do not divide the 64 query rows of a tiled-pass workgroup
     (24, 12, 4, 64, 100, 2, "random"),    # G = 3: 21 tokens x 3 heads per workgroup
     (25, 24, 4, 32, 90, 1, "prefill"),    # G = 6, head_dim 32
@@ -348,6 +352,8 @@ def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
         pos = np.array([90 * (t // 14) + t % 14 + 3 for t in range(tokens)], np.int32)
     elif recipe == "long":
         pos = (2100 + np.arange(tokens)).astype(np.int32)
+    elif recipe == "long9k":
+        pos = (9000 + np.arange(tokens)).astype(np.int32)
     elif recipe == "ring":
         pos = np.array([cap - 1, cap, 2 * cap + 37, 5 * cap + 3] * 3, np.int32)[:tokens] + \
             (synth.randint(111, 5, tokens, 7)).astype(np.int32)
