@@ -92,6 +92,19 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
+def stored_counters(kernel: str, src_hash: str):
+    """Busy fractions from the committed rocprofv3 counter summary, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "valu_busy", "lds_active", "wave_cycles_waiting")}
+
+
 def stored_traffic(kernel: str, src_hash: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when absent or taken on a different kernel source."""
@@ -273,9 +286,50 @@ def run_decode(args, long_context=False):
     achieved = kbytes / (avg_us * 1e-6) / 1e9
     kname = "k_gemv<1,4,1,EPI_SWIGLU,PRO_RMSNORM,1,false>"
     src = source_hash([os.path.join(ROOT, "quantized_q4_q8_amd", "csrc", f)
-                       for f in ("gemv.hip", "internal.h", "common.h")])
+                       for f in ("gemv.hip", "qdot.h", "internal.h", "common.h")])
     traffic = stored_traffic(kname, src)
     log(f"fused gate/up GEMV: {avg_us:.2f} us per launch, {achieved:.0f} GB/s")
+
+    # -- the matmul share of one token: the token's Q4_0 x Q8_0 products
+    #    alone (per layer QKV, output projection, gate/up + SwiGLU and down,
+    #    then the LM head), each a GEMV on a resident Q8_0 activation row,
+    #    back to back in one captured graph
+    Nq, Nqkv = g.n_q_heads * g.head_dim, g.n_qkv
+    xq, xd = qk.quantize_q8_0(xg)
+    hq, hdq = qk.quantize_q8_0(h)
+    y_qkv = torch.empty((1, Nqkv), dtype=torch.float32, device=dev)
+    y_h = torch.empty((1, H), dtype=torch.float32, device=dev)
+    y_lm = torch.empty((1, spec["vocab"]), dtype=torch.float32, device=dev)
+    def matmuls():
+        for lw in dec.layers:
+            qk.qmatmul_q4_0_q8_0(lw.w_qkv_q, lw.w_qkv_d, xq, xd, out=y_qkv)
+            qk.qmatmul_q4_0_q8_0(lw.w_o_q, lw.w_o_d, xq, xd, out=y_h)
+            qk.qk_gate_up_swiglu(lw.w_gate_up_q, lw.w_gate_up_d, xq, xd, out=h)
+            qk.qmatmul_q4_0_q8_0(lw.w_down_q, lw.w_down_d, hq, hdq, out=y_h)
+        qk.qmatmul_q4_0_q8_0(dec.lm_q, dec.lm_d, xq, xd, out=y_lm)
+    mm_us = graph_time_us(matmuls, 1, args.kernel_rounds)
+    mm_bytes = (L * (Nqkv * H + H * Nq + 2 * F * H + H * F) + spec["vocab"] * H) * 9 / 16 \
+        + L * (3 * (H + H // 32 * 2) + F + F // 32 * 2) + H + H // 32 * 2
+    mm_gbs = mm_bytes / (mm_us * 1e-6) / 1e9
+    log(f"matmul step: {mm_us:.1f} us per token, {mm_gbs:.0f} GB/s")
+
+    # -- the attention share of one token: the 22 layers' grouped-query
+    #    attention (chunk and merge passes) over the resident caches at the
+    #    workload's middle position
+    mid = spec["context"] + steps_per_run // 2
+    qa = torch.from_numpy(normal(8, 0, (1, g.n_q_heads, g.head_dim))).to(dev)
+    pa = torch.tensor([mid], dtype=torch.int32, device=dev)
+    oa = torch.empty_like(qa)
+    wsa = torch.empty(qk.load().qk_gqa_attention_workspace(1, g.n_q_heads, g.head_dim, spec["cap"]),
+                      dtype=torch.uint8, device=dev)
+    def attentions():
+        for li in range(L):
+            qk.gqa_attention(qa, dec.k_cache[li], dec.v_cache[li], pa, seq, out=oa, ws=wsa)
+    att_us = graph_time_us(attentions, 1, args.kernel_rounds)
+    att_rows = min(mid + 1, spec["cap"])
+    att_bytes = L * (2 * g.n_kv_heads * g.head_dim * 2 * att_rows + 2 * Nq * 4)
+    att_gbs = att_bytes / (att_us * 1e-6) / 1e9
+    log(f"attention step: {att_us:.1f} us per token ({att_us / L:.2f} us per layer), {att_gbs:.0f} GB/s")
 
     # -- a plain 256 MiB device copy: calibrates the HBM byte counters
     #    (FETCH_SIZE / WRITE_SIZE) of profiling runs against a known size
@@ -319,6 +373,14 @@ def run_decode(args, long_context=False):
                      "avg_us": round(avg_us, 3), "launches_timed": args.kernel_rounds * L,
                      "source_hash": src, "achievable_GBps": round(read_gbs, 1),
                      "frac_of_achievable": round(achieved / read_gbs, 4)},
+        "mul_mat_step": {"what": "the token's Q4_0 x Q8_0 GEMVs alone (22 x QKV, output, gate/up, "
+                                 "down, and the LM head), one graph",
+                         "bytes": int(mm_bytes), "us": round(mm_us, 2), "GBps": round(mm_gbs, 1),
+                         "frac": round(mm_gbs / HBM_PEAK_GBS, 4)},
+        "attention_step": {"what": f"the token's 22 attention calls (chunk + merge) at position {mid}",
+                           "bytes": int(att_bytes), "us": round(att_us, 2),
+                           "us_per_layer": round(att_us / L, 3), "GBps": round(att_gbs, 1),
+                           "frac": round(att_gbs / HBM_PEAK_GBS, 4)},
         "step_roofline": {"bytes_per_token": int(step_bytes),
                           "achieved_GBps": round(step_bytes * tok_s / 1e9, 1),
                           "frac": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -538,6 +600,12 @@ def run_prefill(args):
                        "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                        "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
                        "ops_per_launch": ops, "avg_us": round(us, 2)}
+    gsrc = source_hash([os.path.join(ROOT, "quantized_q4_q8_amd", "csrc", f) for f in ("gemm.hip", "common.h")])
+    out["roofline"]["counters"] = stored_counters("k_gemm_mfma<EPI_SWIGLU>", gsrc)
+    out["gemm_counters"] = {"what": "per-SIMD busy fractions from rocprofv3 counters (MFMA busy at 1.0 = "
+                                    "the int8 peak), null when the GEMM source changed since",
+                            "gate_up": out["roofline"]["counters"],
+                            "qkv_o_down_lm": stored_counters("k_gemm_mfma<EPI_STORE>", gsrc)}
     out["step_roofline"] = {"int_ops_per_step": 2 * lin_macs,
                             "achieved_TOPs": round(2 * lin_macs / (ms / 1e3) / 1e12, 1),
                             "frac": round(2 * lin_macs / (ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4)}
