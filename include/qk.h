@@ -63,7 +63,11 @@ extern "C" {
 #define QK_EWORKSPACE (-4) /* workspace missing or smaller than required */
 #define QK_EHIP (-5)       /* the HIP runtime reported an error */
 
-/* Text for a status code (static storage, never NULL). */
+/* Text for a status code (static storage, never NULL).  [LLAMACPP 5.2-5.4:
+ * the library's C calls report failure through their return value (a null
+ * model, a negative token count, a non-zero decode result); here every call
+ * returns one of the codes above and this call names it.]  Unknown codes
+ * give a generic text. */
 const char* qk_strerror(int status);
 
 /* ---------------------------------------------------------------------- */
@@ -88,9 +92,14 @@ int quantize_q8_0(const float* x, int64_t rows, int64_t k, int8_t* x_q, uint16_t
 int qk_quantize_q4_0(const float* w, int64_t n, int64_t k, uint8_t* w_q, uint16_t* w_d,
                      void* stream);
 
-/* Host helper: convert Q4_0 from interleaved 18-byte blocks (fp16 scale,
- * then 16 nibble bytes; [n][k/32] blocks, host memory) to the split layout
- * (host memory).  Returns QK_ESHAPE when k % 32 != 0. */
+/* Host helper: convert Q4_0 from interleaved 18-byte blocks to the split
+ * layout [GUIDE 6.1: a Q4_0 block is 32 weights, one fp16 scale (2 bytes)
+ * and 32 4-bit codes (16 bytes), 18 bytes in all].  aos18 holds [n][k/32]
+ * blocks, each the fp16 scale followed by the 16 code bytes (byte j: code j
+ * in the low nibble, code j + 16 in the high one), in host memory; w_q and
+ * w_d are host memory too and owned by the caller.  Copies only, no
+ * rounding.  Returns QK_EINVAL for n < 0, k <= 0 or (when n > 0) a null
+ * pointer, and QK_ESHAPE when k % 32 != 0. */
 int qk_q4_0_from_blocks(const void* aos18, int64_t n, int64_t k, uint8_t* w_q, uint16_t* w_d);
 
 /* ---------------------------------------------------------------------- */
@@ -101,7 +110,7 @@ int qk_q4_0_from_blocks(const void* aos18, int64_t n, int64_t k, uint8_t* w_q, u
  * exact int32 block dot isum = sum_{j<32} (c_{r,32b+j} - 8) * x_q[t][32b+j]
  * [LLAMACPP 2.2: y ~ delta * delta_x * sum q q_x, the integer part being pure
  * integer arithmetic; ENGINE 6: C = A B].  W [n][k] Q4_0, x [m][k] Q8_0,
- * y [m][n] fp32 (accumulated in fp32).  m <= 8 runs the decode GEMV, larger
+ * y [m][n] fp32 (accumulated in fp64 and rounded once).  m <= 8 runs the decode GEMV, larger
  * m the int8 MFMA GEMM. */
 int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_t n, int64_t k,
                       const int8_t* x_q, const uint16_t* x_d, int64_t m, float* y,
@@ -115,8 +124,13 @@ int qmatmul_q4_0_q8_0(const uint8_t* w_q, const uint16_t* w_d, int64_t n, int64_
 int qk_gate_up_swiglu(const uint8_t* w_q, const uint16_t* w_d, int64_t ffn, int64_t k,
                       const int8_t* x_q, const uint16_t* x_d, int64_t m, float* h, void* stream);
 
-/* The per-block int32 dot products themselves, for bit-exact checking:
- * isum[t][r][b] for t < m, r < n, b < k/32 (int32 [m][n][k/32]). */
+/* The per-block int32 dot products themselves, for bit-exact checking
+ * [LLAMACPP 2.2: within a block the product of the weight and input codes is
+ * pure integer arithmetic; COLIBRI, System architecture: int8 activations
+ * times int4 weights in integer kernels]: isum[t][r][b] =
+ * sum_{j<32} (c_{r,32b+j} - 8) * x_q[t][32b+j] for t < m, r < n, b < k/32,
+ * int32 [m][n][k/32] (|isum| <= 32 * 8 * 127 = 32512, exact).  The scales
+ * play no part, so none are passed.  Device pointers; k % 32 == 0. */
 int qk_block_dots_q4_0_q8_0(const uint8_t* w_q, int64_t n, int64_t k, const int8_t* x_q,
                             int64_t m, int32_t* isum, void* stream);
 
