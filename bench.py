@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "longctx", "longctx32k", "matmul", "prefill", "moe", "sample"],
+                    choices=["decode", "longctx", "longctx32k", "layer", "matmul", "prefill", "moe",
+                             "sample"],
                     help="decode (the headline line); the others measure decode past an "
                          "8192-row or a 32768-row ring cache and the standalone matmul, "
                          "prefill, MoE and sampler workloads")
@@ -456,6 +457,80 @@ def base_line(args, metric, value, unit, ms_per_step, dtype, config):
 
 
 # ---------------------------------------------------------------------------
+# small layer: H 256, 8/2 heads of 32, F 688 (704), cap 32; a 16-token
+# prefill call, then 16 one-token decode calls (positions 16..31)
+# ---------------------------------------------------------------------------
+def run_layer(args):
+    import numpy as np
+    import torch
+
+    import quantized_q4_q8_amd as qk
+    from quantized_q4_q8_amd.model import layer_to_device
+    from synth import normal
+    from synth import workloads as W
+
+    spec = W.LAYER_SMALL
+    g, P, D, cap = spec["geometry"], spec["prompt"], spec["decode"], spec["cap"]
+    dev = torch.device("cuda")
+    wf = W.layer_weights_f32(spec["seed"], 0, g)
+    lw = layer_to_device(wf)
+    cfg = qk.layer_cfg(**g.cfg(cap))
+    kshape = (1, g.n_kv_heads, cap, g.head_dim)
+    kc = torch.zeros(kshape, dtype=torch.int16, device=dev)
+    vc = torch.zeros(kshape, dtype=torch.int16, device=dev)
+    x0 = normal(spec["seed"], 10, (P, g.hidden))
+    xp = torch.from_numpy(x0).to(dev)
+    xd = torch.from_numpy(x0[-1:].copy()).to(dev)
+    seq_p = torch.zeros(P, dtype=torch.int32, device=dev)
+    seq_d = torch.zeros(1, dtype=torch.int32, device=dev)
+    pos_p = torch.arange(P, dtype=torch.int32, device=dev)
+    pos_d = [torch.tensor([P + j], dtype=torch.int32, device=dev) for j in range(D)]
+    ws = torch.empty(qk.qk_layer_workspace(cfg, P), dtype=torch.uint8, device=dev)
+    rounds = max(20, args.kernel_rounds)
+    pre_us = graph_time_us(lambda: qk.layer_forward(lw, cfg, xp, pos_p, seq_p, kc, vc, ws=ws), 1, rounds)
+    dec_us = graph_time_us(lambda: [qk.layer_forward(lw, cfg, xd, p, seq_d, kc, vc, ws=ws) for p in pos_d],
+                           D, rounds)
+    log(f"layer: prefill call ({P} tokens) {pre_us:.2f} us, decode call {dec_us:.2f} us")
+    H, F, Nq = g.hidden, g.ffn_padded, g.n_q_heads * g.head_dim
+    wbytes = (g.n_qkv * H + H * Nq + 2 * F * H + H * F) * 9 / 16 + 2 * H * 4
+    mid = P + D // 2
+    dbytes = wbytes + 2 * g.n_kv_heads * g.head_dim * 2 * (mid + 1) + 2 * H * 4
+    gbs = dbytes / (dec_us * 1e-6) / 1e9
+    out = base_line(args, "decode layer calls/s, small layer (H 256, 8/2 heads of 32, F 704)",
+                    1e6 / dec_us, "calls/s", dec_us / 1e3, "q4_0 x q8_0 (int32 block dots, fp64 accumulate, fp32 activations)",
+                    {"workload": f"one pre-norm layer, H {H}, heads 8/2 x 32, F {F}, cap {cap}: a {P}-token "
+                                 f"prefill call, then {D} one-token decode calls (positions {P}..{P + D - 1})",
+                     "parallelism": "single GPU"})
+    out["data"] = "synthetic: seeded N(0,0.02) Q4_0 weights, N(0,1) activations"
+    out["prefill_call_us"] = round(pre_us, 2)
+    out["roofline"] = {"bound": "hbm", "kernel": "layer_forward, one decode call (six launches)",
+                       "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                       "bytes_per_launch": int(dbytes), "avg_us": round(dec_us, 3),
+                       "note": "latency-bound: 0.4 MB per call is far below one launch's worth of HBM time"}
+    if not args.no_cpu_baseline:
+        import oracle
+        wl = {}
+        for name, key in [("w_qkv", "w_qkv"), ("w_o", "w_o"), ("w_gate_up", "w_gu"), ("w_down", "w_down")]:
+            wl[key + "_q"], wl[key + "_d"] = oracle.quantize_q4_0(wf[name])
+        wl["gamma_attn"], wl["gamma_ffn"] = wf["gamma_attn"], wf["gamma_ffn"]
+        kh = np.zeros(kshape, np.uint16)
+        vh = np.zeros(kshape, np.uint16)
+        xo = oracle.layer_forward(wl, g.cfg(cap), x0, np.arange(P, dtype=np.int32), np.zeros(P, np.int32), kh, vh)
+        t0, n = time.perf_counter(), 0
+        xr = xo[-1:]
+        while n < D and (time.perf_counter() - t0 < args.cpu_seconds or n == 0):
+            xr = oracle.layer_forward(wl, g.cfg(cap), xr, np.array([P + n], np.int32), np.zeros(1, np.int32), kh, vh)
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        out["cpu_baseline"] = {"value": round(1.0 / dt, 2), "unit": "calls/s", "cores": threads,
+                               "kind": "oracle", "sample": f"{n} oracle decode calls of the same layer "
+                                                           f"(positions {P}..{P + n - 1})"}
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # standalone matmul workload: W 5632x2048 and 2048x5632, batch 1 and 8
 # ---------------------------------------------------------------------------
 def run_matmul(args):
@@ -799,7 +874,7 @@ def main():
     import quantized_q4_q8_amd as qk
     qk.load()
     {"decode": run_decode, "longctx": lambda a: run_decode(a, long_context=True),
-     "longctx32k": lambda a: run_decode(a, long_context="32k"), "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
+     "longctx32k": lambda a: run_decode(a, long_context="32k"), "layer": run_layer, "matmul": run_matmul, "prefill": run_prefill, "moe": run_moe, "sample": run_sample}[args.workload](args)
 
 
 if __name__ == "__main__":
