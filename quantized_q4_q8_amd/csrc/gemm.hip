@@ -20,6 +20,11 @@
 // are staged as fp64, which makes each scaled block sum
 // fma(isum * dx, dw, acc): isum * dx is exact in fp64 (15 + 11 bits) and the
 // fma rounds the exact triple product once.
+//
+// Grouped (the MoE layer's experts): grid z runs over the groups (or over a
+// list of them made on the device), each with its own weights, its columns
+// gathered from the sorted (token, expert) pairs and its outputs in the
+// pairs' order; groups below a column count are left to the grouped GEMV.
 #include "internal.h"
 
 namespace qk {
@@ -74,8 +79,26 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     const int j = lane & 31;
 
     const int64_t k = a.k, nb = k / QBLK, kh = k / 2;
-    const int64_t m = a.m;
+    // grouped: group g = blockIdx.z holds columns cg .. cg + m - 1 (output
+    // rows), gathered from activation rows col_idx[c] (or c); its weights
+    // sit at g * wq_gstride / g * wd_gstride
+    int g = blockIdx.z;
+    if (a.group_list) {   // grid z indexes the list of groups to take
+        if (g >= __builtin_amdgcn_readfirstlane(a.group_list[0])) return;
+        g = __builtin_amdgcn_readfirstlane(a.group_list[1 + g]);
+    }
+    int64_t cg = 0, m = a.m;
+    if (a.col_off) {   // uniform over the workgroup
+        cg = __builtin_amdgcn_readfirstlane(a.col_off[g]);
+        m = __builtin_amdgcn_readfirstlane(a.col_off[g + 1]) - cg;
+        if (m < a.min_cols) return;
+    }
     const int64_t t0 = (int64_t)blockIdx.y * BT;
+    if (t0 >= m) return;
+    const uint8_t* __restrict__ wq = a.wq + (int64_t)g * a.wq_gstride;
+    const uint16_t* __restrict__ wd = a.wd + (int64_t)g * a.wd_gstride;
+    // activation row of local column t (t < m)
+    auto act_row = [&](int64_t t) -> int64_t { return a.col_idx ? (int64_t)a.col_idx[cg + t] : cg + t; };
     // physical weight row of LDS row pr
     const int64_t c0 = (int64_t)blockIdx.x * (EPI == EPI_SWIGLU ? BR / 2 : BR);
     const int64_t nphys = (EPI == EPI_SWIGLU) ? 2 * a.ffn : a.n;
@@ -97,15 +120,25 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     uint4 ra[A_PER], rb[B_PER];
     uint16_t rdah, rdbh[DB_PER];
     bool rda_ok, rdb_ok[DB_PER];
+    // the activation rows this thread stages, looked up once
+    int64_t arow[A_PER], srow;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int64_t t = t0 + ((tid + NT * i) >> 3);
+        arow[i] = t < m ? act_row(t) : -1;
+    }
+    {
+        const int64_t t = t0 + tid % BT;
+        srow = t < m ? act_row(t) : -1;
+    }
     auto gload = [&](int64_t kb0) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int idx = tid + NT * i;          // chunks of 16 B: [token][KB*2]
-            const int tr = idx >> 3, part = idx & 7;
-            const int64_t t = t0 + tr;
+            const int part = idx & 7;
             const int64_t b = kb0 + (part >> 1);
-            if (t < m && b < nb)
-                ra[i] = *reinterpret_cast<const uint4*>(a.xq + t * k + b * QBLK + (part & 1) * 16);
+            if (arow[i] >= 0 && b < nb)
+                ra[i] = *reinterpret_cast<const uint4*>(a.xq + arow[i] * k + b * QBLK + (part & 1) * 16);
             else
                 ra[i] = make_uint4(0, 0, 0, 0);
         }
@@ -115,16 +148,15 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
             const int pr = idx >> 2, bb = idx & 3;
             const int64_t b = kb0 + bb;
             if (prow_valid(pr) && b < nb)
-                rb[i] = *reinterpret_cast<const uint4*>(a.wq + prow_of(pr) * kh + b * 16);
+                rb[i] = *reinterpret_cast<const uint4*>(wq + prow_of(pr) * kh + b * 16);
             else
                 rb[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
         }
         {
-            const int bb = tid / BT, r = tid % BT;   // activation scales [KB][BT]
+            const int bb = tid / BT;   // activation scales [KB][BT]
             const int64_t b = kb0 + bb;
-            const int64_t t = t0 + r;
-            rda_ok = t < m && b < nb;
-            rdah = a.xd[rda_ok ? t * nb + b : 0];
+            rda_ok = srow >= 0 && b < nb;
+            rdah = a.xd[rda_ok ? srow * nb + b : 0];
         }
 #pragma unroll
         for (int i = 0; i < DB_PER; ++i) {
@@ -132,7 +164,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
             const int bb = idx / BR, r = idx % BR;
             const int64_t b = kb0 + bb;
             rdb_ok[i] = prow_valid(r) && b < nb;
-            rdbh[i] = a.wd[rdb_ok[i] ? prow_of(r) * nb + b : 0];
+            rdbh[i] = wd[rdb_ok[i] ? prow_of(r) * nb + b : 0];
         }
     };
     auto sstore = [&](Stage& s) {
@@ -222,7 +254,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t t = t0 + wt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-            const int64_t tc = t < m ? t : m - 1;
+            const int64_t tc = cg + (t < m ? t : m - 1);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const int pr = lds_col(cb);
@@ -243,22 +275,26 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
                 const int64_t r = prow_of(pr);
                 float val = (float)acc[cb][v];
                 if (a.residual) val = rv[cb][v] + val;
-                a.y[t * a.ldy + r] = val;
+                a.y[(cg + t) * a.ldy + r] = val;
             }
         } else {
             const int64_t f = c0 + wc * 32 + j;
-            if (f < a.ffn) a.y[t * a.ldy + f] = swiglu1((float)acc[0][v], (float)acc[1][v]);
+            if (f < a.ffn) a.y[(cg + t) * a.ldy + f] = swiglu1((float)acc[0][v], (float)acc[1][v]);
         }
     }
 }
 
-int launch_gemm(const GemvArgs& a, int epi, hipStream_t s) {
-    const unsigned gt = (unsigned)((a.m + BT - 1) / BT);
+int launch_gemm(const GemvArgs& a, int epi, hipStream_t s, int64_t max_group_cols,
+                int64_t max_groups) {
+    const int64_t cols = a.col_off ? max_group_cols : (int64_t)a.m;
+    const unsigned gt = (unsigned)((cols + BT - 1) / BT);
+    const unsigned gz = !a.col_off ? 1u : (a.group_list ? (unsigned)max_groups : (unsigned)a.groups);
+    if (gt == 0 || gz == 0) return QK_OK;
     if (epi == EPI_SWIGLU) {
-        dim3 grid((unsigned)((a.ffn + BR / 2 - 1) / (BR / 2)), gt);
+        dim3 grid((unsigned)((a.ffn + BR / 2 - 1) / (BR / 2)), gt, gz);
         hipLaunchKernelGGL(k_gemm_mfma<EPI_SWIGLU>, grid, dim3(NT), 0, s, a);
     } else {
-        dim3 grid((unsigned)((a.n + BR - 1) / BR), gt);
+        dim3 grid((unsigned)((a.n + BR - 1) / BR), gt, gz);
         hipLaunchKernelGGL(k_gemm_mfma<EPI_STORE>, grid, dim3(NT), 0, s, a);
     }
     return qk_launch_status();

@@ -194,6 +194,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a) {
         nc = __builtin_amdgcn_readfirstlane(a.col_off[g + 1]) - c0;
     }
     if (nc <= 0) return;   // uniform over the workgroup
+    if (a.skip_cols_ge > 0 && nc >= a.skip_cols_ge) return;   // the grouped MFMA GEMM's share
 
     const int64_t k = a.k, nb = k / QBLK;
     constexpr uint32_t BB = FMT == FMT_Q2_ROW ? 8u : 16u;   // weight bytes per 32-block

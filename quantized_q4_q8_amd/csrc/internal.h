@@ -65,6 +65,14 @@ struct GemvArgs {
     // EPI_ARGMAX: partials [column][workgroup]
     float* part_val;
     int32_t* part_idx;
+    // grouped launches (col_off set): the GEMV leaves groups of at least
+    // skip_cols_ge columns (0: none) to the grouped MFMA GEMM, which takes
+    // only groups of at least min_cols columns
+    int32_t skip_cols_ge;
+    int32_t min_cols;
+    // grouped MFMA GEMM: [0] = n, [1 .. n] = the groups to take (grid z
+    // indexes this list; null: grid z is the group)
+    const int32_t* group_list;
 };
 
 // Launch the GEMV with the given epilogue and prologue; returns QK_ESHAPE when
@@ -83,9 +91,15 @@ int64_t gemv_argmax_parts(int64_t n, int64_t k, int64_t max_cols);
 int launch_quantize_q8(const float* x, int64_t rows, int64_t k, int8_t* xq, uint16_t* xd,
                        hipStream_t s);
 
-// MFMA GEMM for many columns (prefill).  Same argument meaning as GemvArgs
-// without grouping (col_off must be null).
-int launch_gemm(const GemvArgs& a, int epi, hipStream_t s);
+// MFMA GEMM for many columns (prefill).  Same argument meaning as GemvArgs.
+// Q4_0 weights only.  Grouped (col_off set, `groups` groups): group g's
+// columns are col_off[g] .. col_off[g + 1] - 1, its activation rows
+// col_idx[c] (or c), its output rows c, its weights at g * wq_gstride /
+// g * wd_gstride; groups of fewer than min_cols columns are skipped, and
+// max_group_cols bounds every group's column count, and with group_list
+// max_groups bounds its length (they size the grid).
+int launch_gemm(const GemvArgs& a, int epi, hipStream_t s, int64_t max_group_cols = 0,
+                int64_t max_groups = 0);
 
 // y = rmsnorm(x) rows; optional Q8_0 of y into (xq, xd); y may be null.
 int launch_rmsnorm_q8(const float* x, const float* gamma, int64_t rows, int64_t dim, float eps,

@@ -14,8 +14,11 @@
 //     weights normalized over the selection;
 //  3. stable counting sort of the (token, rank) pairs by expert -> per-expert
 //     column ranges, the token of every sorted column, and each pair's slot;
-//  4. Q8_0 of x; grouped gate/up GEMV with the SwiGLU epilogue over the
-//     sorted columns; Q8_0 of h; grouped down GEMV;
+//  4. Q8_0 of x; grouped gate/up matmul with the SwiGLU epilogue over the
+//     sorted columns; Q8_0 of h; grouped down matmul.  In calls averaging
+//     at least 16 tokens per expert (Q4_0 experts), an expert with at least
+//     16 tokens runs on the int8 matrix cores (grouped MFMA GEMM) and the
+//     others on the grouped GEMV; otherwise the GEMV takes them all;
 //  5. per token, sum over ranks 0..k-1 of weight * expert output, in order.
 #include "internal.h"
 
@@ -25,6 +28,8 @@ namespace {
 
 constexpr int RT = 4;        // tokens per router workgroup
 constexpr int RSLICE = 128;  // hidden elements per router slice: all its loads issue together
+constexpr int MFMA_MIN_COLS = 16;   // tokens from which an expert takes the grouped MFMA GEMM
+constexpr int MFMA_MIN_AVG = 16;    // ... when the call averages this many tokens per expert
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -33,6 +38,7 @@ struct MoeWs {
     int32_t* off;       // [E + 1]
     int32_t* col_tok;   // [P] token of each sorted column
     int32_t* slot;      // [P] sorted column of pair p = t * k + rank
+    int32_t* big;       // [1 + E]: the count, then the experts of at least MFMA_MIN_COLS tokens
     int8_t* xq;         // [T][H]
     uint16_t* xd;       // [T][H/32]
     float* h;           // [P][F]
@@ -56,6 +62,7 @@ MoeWs moe_layout(void* base, int64_t T, int64_t H, int64_t E, int64_t k, int64_t
     w.off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
     w.col_tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
     w.slot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * P));
+    w.big = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
     w.xq = reinterpret_cast<int8_t*>(take((size_t)(T * H)));
     w.xd = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * T * (H / QBLK)));
     w.h = reinterpret_cast<float*>(take(sizeof(float) * P * F));
@@ -210,16 +217,22 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ rpart,
 __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ sel_idx, int64_t P,
                                                 int32_t k, int64_t E, int32_t* __restrict__ off,
                                                 int32_t* __restrict__ col_tok,
-                                                int32_t* __restrict__ slot) {
+                                                int32_t* __restrict__ slot, int32_t* __restrict__ big,
+                                                int min_cols) {
     __shared__ int cnt[1024];
     __shared__ int base[1024];
     __shared__ __align__(16) int chunk_e[1024];
     __shared__ int wsum[16];
+    __shared__ int nbig;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < E) cnt[tid] = 0;
+    if (tid == 0) nbig = 0;
     __syncthreads();
     for (int64_t p = tid; p < P; p += 1024) atomicAdd(&cnt[sel_idx[p]], 1);
     __syncthreads();
+    // the experts with at least min_cols tokens, in any order (each one's
+    // result does not depend on the others)
+    if (tid < E && cnt[tid] >= min_cols) big[1 + atomicAdd(&nbig, 1)] = tid;
     // exclusive scan of the counts: inclusive within each wave, then the
     // totals of the waves before
     const int c = tid < E ? cnt[tid] : 0;
@@ -240,6 +253,7 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ sel_
         if (tid == E - 1) off[E] = excl + c;
     }
     __syncthreads();
+    if (tid == 0) big[0] = nbig;
     for (int64_t c0 = 0; c0 < P; c0 += 1024) {
         const int64_t p = c0 + tid;
         const int n = (int)min((int64_t)1024, P - c0);
@@ -327,7 +341,7 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(1024), 0, s, w.rpart, slices, T, E, top_k,
                        sel_idx, sel_w);
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, sel_idx, P, top_k, E, w.off, w.col_tok,
-                       w.slot);
+                       w.slot, w.big, MFMA_MIN_COLS);
     int rc = launch_quantize_q8(x, T, H, w.xq, w.xd, s);
     if (rc) return rc;
 
@@ -342,8 +356,23 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     g.xq = w.xq; g.xd = w.xd; g.col_off = w.off; g.col_idx = w.col_tok;
     g.m = 0; g.groups = (int32_t)E; g.y = w.h; g.ldy = F; g.residual = nullptr; g.ldr = 0;
     g.ffn = F; g.max_cols = (int32_t)std::min<int64_t>(8, (P + E - 1) / E);
+    // Experts with at least MFMA_MIN_COLS tokens run on the int8 matrix
+    // cores (grouped GEMM), the others on the grouped GEMV; the split is read
+    // from the grouping on the device, so both launches go out and each
+    // skips the other's experts.  An expert has at most T tokens.
+    // The GEMM's grid covers the list of such experts that the grouping
+    // writes: at most P / MFMA_MIN_COLS of them.  Below an average of
+    // MFMA_MIN_AVG tokens per expert few experts are that large, and the two
+    // launches cost more than they save (1.5 % of a 64-token, 256-expert
+    // layer that has none, 1.2 % at 256 tokens): the GEMV takes every expert.
+    const bool mfma = ew.fmt == FMT_Q4_0 && T >= MFMA_MIN_COLS && P >= (int64_t)MFMA_MIN_AVG * E;
+    const int64_t max_big = std::min<int64_t>(E, P / MFMA_MIN_COLS);
+    g.skip_cols_ge = mfma ? MFMA_MIN_COLS : 0;
+    g.min_cols = MFMA_MIN_COLS;
+    g.group_list = w.big;
     rc = launch_gemv(g, EPI_SWIGLU, s);
     if (rc) return rc;
+    if (mfma && (rc = launch_gemm(g, EPI_SWIGLU, s, T, max_big))) return rc;
     rc = launch_quantize_q8(w.h, P, F, w.hq, w.hd, s);
     if (rc) return rc;
 
@@ -358,8 +387,12 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     d.xq = w.hq; d.xd = w.hd; d.col_off = w.off; d.col_idx = nullptr;
     d.m = 0; d.groups = (int32_t)E; d.y = w.ys; d.ldy = H; d.residual = nullptr; d.ldr = 0;
     d.ffn = 0; d.max_cols = g.max_cols;
+    d.skip_cols_ge = g.skip_cols_ge;
+    d.min_cols = MFMA_MIN_COLS;
+    d.group_list = w.big;
     rc = launch_gemv(d, EPI_STORE, s);
     if (rc) return rc;
+    if (mfma && (rc = launch_gemm(d, EPI_STORE, s, T, max_big))) return rc;
 
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, s,
                        w.ys, H, top_k, w.slot, sel_w, y);

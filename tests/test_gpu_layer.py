@@ -323,6 +323,49 @@ def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     assert np.allclose(w_g.sum(1), 1.0, atol=1e-6)
 
 
+@pytest.mark.parametrize("T,H,E,F,k,skew", [
+    (256, 256, 8, 128, 2, False),   # about 64 tokens per expert: every expert on the matrix cores
+    (96, 256, 16, 64, 4, True),     # experts 0 and 1 take every token, the rest about 14 each: both paths
+    (64, 6144, 16, 512, 8, False),  # the MoE workload's hidden width, 32 tokens per expert
+])
+def test_moe_mfma_experts(gpu_lib, T, H, E, F, k, skew):
+    """Experts with at least 16 tokens run on the grouped int8 MFMA GEMM, the
+    others on the grouped GEMV (calls averaging at least 16 tokens per
+    expert); every token's output matches the oracle's.
+    skew: a router that always ranks experts 0 and 1 first (a large constant
+    feature and router weights on it), so that two experts hold every token
+    and the others few."""
+    qk = gpu_lib
+    say(f"moe_route_and_apply (matrix-core experts) T={T} H={H} E={E} F={F} k={k} skew={skew}")
+    seed = 70 + T
+    x = synth.normal(seed, W.TID_X, (T, H))
+    wr = synth.normal(seed, W.TID_ROUTER, (H, E), 0.02)
+    if skew:
+        x[:, 0] = 8.0
+        wr[0, :] = 0.0
+        wr[0, 0], wr[0, 1] = 1.0, 0.9
+    gu, dn = experts_f32(seed, E, H, F)
+    guq = np.stack([oracle.quantize_q4_0(a)[0] for a in gu])
+    gud = np.stack([oracle.quantize_q4_0(a)[1] for a in gu])
+    dnq = np.stack([oracle.quantize_q4_0(a)[0] for a in dn])
+    dnd = np.stack([oracle.quantize_q4_0(a)[1] for a in dn])
+    del gu, dn
+    out, sel, w = oracle.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd)
+    _, _, logits = oracle.moe_route(x, wr, k, return_logits=True)
+    counts = np.bincount(sel.ravel(), minlength=E)
+    assert counts.max() >= 16, "the case must give some expert the matrix-core path"
+    if skew:
+        assert counts.min() < 16
+    y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
+    sel_g, w_g = host(sg), host(wg)
+    check_routing(sel_g, w_g, sel, w, logits)
+    want = moe_expected(sel_g, w_g, sel, out, logits,
+                        lambda t, e: oracle.moe_expert_ffn(x[t], guq[e], gud[e], dnq[e], dnd[e]))
+    assert rel_err(host(y), want) < LAYER_TOL
+    if np.array_equal(sel_g, sel):
+        assert_same_fp32(host(y), out)
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (16, 6144, 16, 2048, 8)])
 def test_moe_rowq_matches_oracle(gpu_lib, bits, T, H, E, F, k):
