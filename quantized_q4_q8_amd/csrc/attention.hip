@@ -172,26 +172,31 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
 // per chunk, and longer contexts load their further pairs PB at a time.  A
 // thread adds its chunks in order and the slice sums are added in slice
 // order, so the result does not depend on timing.  Writes the fp32 output
-// and/or its Q8_0 codes (four lanes per block).
-template <int HD>
+// and/or its Q8_0 codes (four lanes per block).  SPLIT > 1 (long contexts):
+// the head's dims are split over SPLIT workgroups (grid z), each a whole
+// number of Q8_0 blocks; every split forms the same chunk weights.
+template <int HD, int SPLIT>
 __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ rec, int64_t nq,
                                                     int64_t nch, int64_t cap,
                                                     const int32_t* __restrict__ pos,
                                                     float* __restrict__ out, int64_t o_ts,
                                                     int8_t* __restrict__ oq,
                                                     uint16_t* __restrict__ od) {
-    constexpr int PAIRS = HD / 2;
+    constexpr int DH = HD / SPLIT;   // dims of this workgroup
+    constexpr int PAIRS = DH / 2;
     constexpr int SLICES = 256 / PAIRS;
     constexpr int PB = 16;   // output pairs per thread per round of loads
     static_assert(MAX_CHUNKS == 512, "(m, l) of two chunks per thread");
+    static_assert(DH % QBLK == 0, "whole Q8_0 blocks per workgroup");
     __shared__ double wsh[MAX_CHUNKS];
     __shared__ double red[4];
     __shared__ double2 acc_s[SLICES][PAIRS];
-    __shared__ double res[HD];
+    __shared__ double res[DH];
     const int64_t h = blockIdx.x, t = blockIdx.y;
+    const int d0 = (int)blockIdx.z * DH;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
-    const int64_t col = h * HD;
+    const int64_t col = h * HD + d0;
     const bool valid = p >= 0;   // negative position: zeros, no reads
     const int used = valid ? (int)(min((int64_t)p, cap - 1) / ACH) + 1 : 0;
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
 #pragma unroll
         for (int e = 0; e < PB; ++e) {
             const int cc = sl + (e0 + e) * SLICES;
-            xv[e] = cc < used ? *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + 2 * pr)
+            xv[e] = cc < used ? *reinterpret_cast<const double2*>(hr + cc * (HD + 2) + 2 + d0 + 2 * pr)
                               : make_double2(0.0, 0.0);
         }
     };
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
         res[2 * tid + 1] = valid ? s1 / lsum : 0.0;
     }
     __syncthreads();
-    if (tid < HD / 8) {   // four lanes per Q8_0 block
+    if (tid < DH / 8) {   // four lanes per Q8_0 block
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (float)res[8 * tid + e];
@@ -550,13 +555,17 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     if (hd == 32) {
         hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                            pos, seq, rec, nch);
-        hipLaunchKernelGGL(k_attn_merge<32>, mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
+        hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
                            o_ts, oq, od);
     } else if (hd == 64) {
         hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                            pos, seq, rec, nch);
-        hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
-                           o_ts, oq, od);
+        if (nch > 64)   // long contexts: two workgroups per head, 32 dims each
+            hipLaunchKernelGGL((k_attn_merge<64, 2>), dim3((unsigned)nq, (unsigned)tokens, 2u), dim3(256), 0,
+                               s, rec, nq, nch, cap, pos, out, o_ts, oq, od);
+        else
+            hipLaunchKernelGGL((k_attn_merge<64, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
+                               o_ts, oq, od);
     } else {
         return QK_ESHAPE;
     }
