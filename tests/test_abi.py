@@ -96,3 +96,37 @@ def test_scratch_size_constant_matches_header():
     """The binding's QK_SCRATCH_BYTES is the header's."""
     m = re.search(r"#define QK_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == qk.QK_SCRATCH_BYTES
+
+
+def test_decode_greedy_validation_host_only(lib):
+    """qk_decode_greedy checks its arguments on the host before it touches the
+    device: missing pointers, too many layers, a logits buffer without rows
+    and misaligned tables give their codes, and zero tokens return at once."""
+    cfg = qk.layer_cfg(hidden=2048, n_q_heads=32, n_kv_heads=4, head_dim=64, ffn=5632,
+                       eps=1e-5, rope_base=1e4, cap=2176)
+    fake = 4096   # never dereferenced: every call below returns before any device work
+
+    def dec(**kw):
+        f = dict(layers=fake, n_layers=22, embed=fake, gamma_final=fake, lm_q=fake, lm_d=fake,
+                 vocab=32000, k_cache=fake, v_cache=fake)
+        f.update(kw)
+        return qk.DecoderStruct(**f)
+
+    def call(m, n_tokens=4, first=fake, forced=None, out=fake, logits=None, rows=0):
+        return lib.qk_decode_greedy(ctypes.byref(m) if m is not None else None, ctypes.byref(cfg),
+                                    first, forced, 2048, n_tokens, out, logits, rows, 0, None, 0, None)
+
+    assert call(None) == qk.QK_EINVAL
+    assert call(dec(n_layers=0)) == qk.QK_EINVAL
+    assert call(dec(n_layers=65)) == qk.QK_ESHAPE           # more layers than the kernel's table holds
+    assert call(dec(), n_tokens=0) == qk.QK_OK               # nothing to do, nothing enqueued
+    assert call(dec(), n_tokens=-1) == qk.QK_EINVAL
+    assert call(dec(embed=None)) == qk.QK_EINVAL
+    assert call(dec(), out=None) == qk.QK_EINVAL
+    assert call(dec(), first=None, forced=None) == qk.QK_EINVAL   # no first id and no forced ids
+    assert call(dec(), logits=fake, rows=0) == qk.QK_EINVAL
+    assert call(dec(embed=fake + 4)) == qk.QK_EALIGN
+    assert lib.qk_decode_workspace(None) == 0
+    flag = ctypes.c_int32(7)
+    assert lib.qk_decode_error(None, ctypes.byref(cfg), ctypes.byref(flag)) == qk.QK_EINVAL
+    assert flag.value == 7
