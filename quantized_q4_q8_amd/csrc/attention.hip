@@ -270,6 +270,45 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     }
 }
 
+// Longest-first order of the tiled pass's token tiles (TQ tokens each): a
+// tile's cost is the number of 64-row chunks its furthest position attends,
+// and order[] lists the tiles by cost, largest first (a counting sort; the
+// order within a cost does not matter, every tile's result is its own).
+// Dispatched in token order, the costliest tiles of a causal prefill (the
+// last tokens of each sequence) started last and left most of the chip idle
+// in the kernel's tail.
+__global__ __launch_bounds__(1024) void k_tile_order(const int32_t* __restrict__ pos, int64_t tokens,
+                                                     int tq, int64_t cap, int ntiles,
+                                                     int32_t* __restrict__ order) {
+    __shared__ int cnt[MAX_CHUNKS + 1];
+    __shared__ int base[MAX_CHUNKS + 1];
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= MAX_CHUNKS; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    auto cost = [&](int tile) {
+        int kmax = -1;
+        for (int j = 0; j < tq; ++j) {
+            const int64_t t = (int64_t)tile * tq + j;
+            if (t < tokens) {
+                const int p = pos[t];
+                if (p >= 0) kmax = max(kmax, (int)min((int64_t)p, cap - 1));
+            }
+        }
+        return kmax >= 0 ? kmax / ACH + 1 : 0;   // <= MAX_CHUNKS
+    };
+    for (int tile = tid; tile < ntiles; tile += 1024) atomicAdd(&cnt[cost(tile)], 1);
+    __syncthreads();
+    if (tid == 0) {   // base[c]: the tiles that cost more than c
+        int run = 0;
+        for (int c = MAX_CHUNKS; c >= 0; --c) {
+            base[c] = run;
+            run += cnt[c];
+        }
+    }
+    __syncthreads();
+    for (int tile = tid; tile < ntiles; tile += 1024) order[atomicAdd(&base[cost(tile)], 1)] = tile;
+}
+
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 // Attention for many tokens on the fp64 matrix cores (v_mfma_f64_16x16x4f64).
@@ -298,7 +337,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_flash_mfma(
     const float* __restrict__ q, int64_t q_ts, int64_t tokens, int64_t nq, int64_t nkv,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, float* __restrict__ out,
-    int64_t o_ts, int8_t* __restrict__ oq, uint16_t* __restrict__ od) {
+    int64_t o_ts, int8_t* __restrict__ oq, uint16_t* __restrict__ od,
+    const int32_t* __restrict__ order) {
     constexpr int NS = HD / 4;     // k-steps of the score product (dims)
     constexpr int NDT = HD / 16;   // dim tiles of the output
     constexpr int KS = HD + 4, VS = HD + 4;
@@ -309,7 +349,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_flash_mfma(
 
     const int G = (int)(nq / nkv);
     const int TQ = 64 / G;   // tokens per workgroup
-    const int64_t g = blockIdx.y, t0 = (int64_t)blockIdx.x * TQ;
+    // workgroup rank * nkv + KV head: the tile of that rank in the
+    // longest-first order, every KV head of a tile one after another, so
+    // that the tiles that walk the most chunks start first
+    const int64_t g = blockIdx.x % nkv;
+    const int64_t t0 = (int64_t)__builtin_amdgcn_readfirstlane(order[blockIdx.x / nkv]) * TQ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ntile = (int)min((int64_t)TQ, tokens - t0);
     const int qr = 16 * wave + (lane & 15);            // this lane's query row
@@ -537,16 +581,22 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     const int64_t nch = (cap + ACH - 1) / ACH;
     if (nch > MAX_CHUNKS || (nq / nkv) * hd > 512) return QK_ESHAPE;
     if (tokens > FLASH_MIN_TOKENS) {
+        if (hd != 32 && hd != 64) return QK_ESHAPE;
         const int64_t tq = 64 / (nq / nkv);   // tokens per workgroup of the matrix-core pass
-        dim3 fgrid((unsigned)((tokens + tq - 1) / tq), (unsigned)nkv);
+        const int64_t ntiles = (tokens + tq - 1) / tq;
+        if (ntiles * nkv > INT32_MAX) return QK_ESHAPE;
+        // the tile order sits at the start of the workspace (the chunk
+        // records of the few-token pass are not used here; they take at
+        // least 34 bytes per token, the order 4 per tile)
+        int32_t* order = static_cast<int32_t*>(ws);
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, s, pos, tokens, (int)tq, cap, (int)ntiles, order);
+        dim3 fgrid((unsigned)(nkv * ntiles));
         if (hd == 32)
             hipLaunchKernelGGL(k_attn_flash_mfma<32>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
-                               kc, vc, cap, pos, seq, out, o_ts, oq, od);
-        else if (hd == 64)
-            hipLaunchKernelGGL(k_attn_flash_mfma<64>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
-                               kc, vc, cap, pos, seq, out, o_ts, oq, od);
+                               kc, vc, cap, pos, seq, out, o_ts, oq, od, order);
         else
-            return QK_ESHAPE;
+            hipLaunchKernelGGL(k_attn_flash_mfma<64>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
+                               kc, vc, cap, pos, seq, out, o_ts, oq, od, order);
         return qk_launch_status();
     }
     double* rec = static_cast<double*>(ws);
