@@ -278,35 +278,56 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
 // last tokens of each sequence) started last and left most of the chip idle
 // in the kernel's tail.
 __global__ __launch_bounds__(1024) void k_tile_order(const int32_t* __restrict__ pos, int64_t tokens,
-                                                     int tq, int64_t cap, int ntiles,
+                                                     int tq, int64_t cap, int nch, int ntiles,
                                                      int32_t* __restrict__ order) {
+    constexpr int KEEP = 4;   // tiles per thread whose cost is kept in registers
     __shared__ int cnt[MAX_CHUNKS + 1];
     __shared__ int base[MAX_CHUNKS + 1];
     const int tid = threadIdx.x;
-    for (int i = tid; i <= MAX_CHUNKS; i += 1024) cnt[i] = 0;
-    __syncthreads();
+    for (int i = tid; i <= nch; i += 1024) cnt[i] = 0;
+    // a tile's positions are read eight at a time from clamped indexes, so
+    // that their loads are in flight together
     auto cost = [&](int tile) {
         int kmax = -1;
-        for (int j = 0; j < tq; ++j) {
-            const int64_t t = (int64_t)tile * tq + j;
-            if (t < tokens) {
-                const int p = pos[t];
-                if (p >= 0) kmax = max(kmax, (int)min((int64_t)p, cap - 1));
+        for (int j0 = 0; j0 < tq; j0 += 8) {
+            int p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t t = (int64_t)tile * tq + j0 + j;
+                p[j] = (j0 + j < tq && t < tokens) ? pos[t] : -1;
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (p[j] >= 0) kmax = max(kmax, (int)min((int64_t)p[j], cap - 1));
         }
         return kmax >= 0 ? kmax / ACH + 1 : 0;   // <= MAX_CHUNKS
     };
-    for (int tile = tid; tile < ntiles; tile += 1024) atomicAdd(&cnt[cost(tile)], 1);
+    int kept[KEEP];
+#pragma unroll
+    for (int i = 0; i < KEEP; ++i) {
+        const int tile = tid + 1024 * i;
+        kept[i] = tile < ntiles ? cost(tile) : 0;
+    }
     __syncthreads();
-    if (tid == 0) {   // base[c]: the tiles that cost more than c
+#pragma unroll
+    for (int i = 0; i < KEEP; ++i)
+        if (tid + 1024 * i < ntiles) atomicAdd(&cnt[kept[i]], 1);
+    for (int tile = tid + 1024 * KEEP; tile < ntiles; tile += 1024) atomicAdd(&cnt[cost(tile)], 1);
+    __syncthreads();
+    if (tid == 0) {   // base[c]: the tiles that cost more than c (costs are at most nch)
         int run = 0;
-        for (int c = MAX_CHUNKS; c >= 0; --c) {
+        for (int c = nch; c >= 0; --c) {
             base[c] = run;
             run += cnt[c];
         }
     }
     __syncthreads();
-    for (int tile = tid; tile < ntiles; tile += 1024) order[atomicAdd(&base[cost(tile)], 1)] = tile;
+#pragma unroll
+    for (int i = 0; i < KEEP; ++i) {
+        const int tile = tid + 1024 * i;
+        if (tile < ntiles) order[atomicAdd(&base[kept[i]], 1)] = tile;
+    }
+    for (int tile = tid + 1024 * KEEP; tile < ntiles; tile += 1024) order[atomicAdd(&base[cost(tile)], 1)] = tile;
 }
 
 typedef double v4d __attribute__((ext_vector_type(4)));
@@ -589,7 +610,8 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
         // records of the few-token pass are not used here; they take at
         // least 34 bytes per token, the order 4 per tile)
         int32_t* order = static_cast<int32_t*>(ws);
-        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, s, pos, tokens, (int)tq, cap, (int)ntiles, order);
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, s, pos, tokens, (int)tq, cap, (int)nch,
+                           (int)ntiles, order);
         dim3 fgrid((unsigned)(nkv * ntiles));
         if (hd == 32)
             hipLaunchKernelGGL(k_attn_flash_mfma<32>, fgrid, dim3(256), 0, s, q, q_ts, tokens, nq, nkv,
