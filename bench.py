@@ -426,10 +426,10 @@ def cpu_decode_baseline(spec, host, first, budget_s: float):
                       f"fp64/exact-int C++ with OpenMP"}
 
 
-def graph_time_us(fn, launches: int, rounds: int) -> float:
+def graph_time_us(fn, launches: int, rounds: int, warm: int = 1) -> float:
     """Average µs per launch of `fn` (which makes `launches` launches),
-    captured once in a graph and replayed `rounds` times; HIP events on the
-    replay stream."""
+    captured once in a graph, replayed `warm` times untimed and then `rounds`
+    times timed; HIP events on the replay stream."""
     import torch
 
     fn()
@@ -437,7 +437,8 @@ def graph_time_us(fn, launches: int, rounds: int) -> float:
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
-    g.replay()
+    for _ in range(max(1, warm)):
+        g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -758,7 +759,10 @@ def run_moe(args):
     call()
     torch.cuda.synchronize()
     distinct = int(torch.unique(sel).numel())
-    us = graph_time_us(call, 1, max(3, args.steps))
+    # A layer takes about 1 ms: a few replays would time the clocks settling
+    # under the sustained load as much as the layer, so the line times 20 (or
+    # --steps) after 10 (or --warmup) untimed ones.
+    us = graph_time_us(call, 1, max(20, args.steps), warm=max(10, args.warmup))
     nbytes = distinct * per_expert + H * E * 4 + 2 * T * H * 4
     gbs = nbytes / us / 1e3
     log(f"moe ({args.codec}): {us:.1f} us per layer, {distinct} distinct experts of {per_expert} B, "

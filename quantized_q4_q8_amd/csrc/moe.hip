@@ -370,7 +370,7 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     g.skip_cols_ge = mfma ? MFMA_MIN_COLS : 0;
     g.min_cols = MFMA_MIN_COLS;
     g.group_list = w.big;
-    rc = launch_gemv(g, EPI_SWIGLU, s);
+    rc = expert_gemv_fits(g) ? launch_expert_gemv(g, EPI_SWIGLU, s) : launch_gemv(g, EPI_SWIGLU, s);
     if (rc) return rc;
     if (mfma && (rc = launch_gemm(g, EPI_SWIGLU, s, T, max_big))) return rc;
     rc = launch_quantize_q8(w.h, P, F, w.hq, w.hd, s);
@@ -390,7 +390,7 @@ int moe_apply(const float* x, int64_t tokens, int64_t hidden, const float* w_rou
     d.skip_cols_ge = g.skip_cols_ge;
     d.min_cols = MFMA_MIN_COLS;
     d.group_list = w.big;
-    rc = launch_gemv(d, EPI_STORE, s);
+    rc = expert_gemv_fits(d) ? launch_expert_gemv(d, EPI_STORE, s) : launch_gemv(d, EPI_STORE, s);
     if (rc) return rc;
     if (mfma && (rc = launch_gemm(d, EPI_STORE, s, T, max_big))) return rc;
 

@@ -366,6 +366,42 @@ def test_moe_mfma_experts(gpu_lib, T, H, E, F, k, skew):
         assert_same_fp32(host(y), out)
 
 
+@pytest.mark.parametrize("T,H,E,F,k", [
+    (12, 6144, 4, 544, 4),   # every expert holds all 12 tokens: gate/up columns staged 5, 5, 2
+    (15, 2048, 8, 96, 3),    # 3 to 8 tokens per expert, 3-block down rows, one row group per workgroup
+])
+def test_moe_expert_gemv_stages(gpu_lib, T, H, E, F, k):
+    """The grouped expert GEMV (fewer than 16 tokens per call on average, so
+    no expert goes to the matrix cores) on experts with more columns than it
+    stages at once (five at hidden 6144), with an odd number of blocks per
+    down row (17 at ffn 544: the scale's half of its 32-bit word changes from
+    row to row), and with workgroups that take one or two row groups after
+    their pairs; every token matches the oracle."""
+    qk = gpu_lib
+    say(f"moe_route_and_apply (expert GEMV column stages) T={T} H={H} E={E} F={F} k={k}")
+    seed = 90 + T
+    x = synth.normal(seed, W.TID_X, (T, H))
+    wr = synth.normal(seed, W.TID_ROUTER, (H, E), 0.02)
+    gu, dn = experts_f32(seed, E, H, F)
+    guq = np.stack([oracle.quantize_q4_0(a)[0] for a in gu])
+    gud = np.stack([oracle.quantize_q4_0(a)[1] for a in gu])
+    dnq = np.stack([oracle.quantize_q4_0(a)[0] for a in dn])
+    dnd = np.stack([oracle.quantize_q4_0(a)[1] for a in dn])
+    del gu, dn
+    out, sel, w = oracle.moe_route_and_apply(x, wr, k, guq, gud, dnq, dnd)
+    _, _, logits = oracle.moe_route(x, wr, k, return_logits=True)
+    counts = np.bincount(sel.ravel(), minlength=E)
+    assert counts.max() > 5 and counts.max() < 16, "some expert needs several column stages"
+    y, sg, wg = qk.moe_route_and_apply(dev(x), dev(wr), k, dev(guq), dev(gud), dev(dnq), dev(dnd))
+    sel_g, w_g = host(sg), host(wg)
+    check_routing(sel_g, w_g, sel, w, logits)
+    want = moe_expected(sel_g, w_g, sel, out, logits,
+                        lambda t, e: oracle.moe_expert_ffn(x[t], guq[e], gud[e], dnq[e], dnd[e]))
+    assert rel_err(host(y), want) < LAYER_TOL
+    if np.array_equal(sel_g, sel):
+        assert_same_fp32(host(y), out)
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (16, 6144, 16, 2048, 8)])
 def test_moe_rowq_matches_oracle(gpu_lib, bits, T, H, E, F, k):
