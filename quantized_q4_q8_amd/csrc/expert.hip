@@ -21,6 +21,11 @@
 // fma(dw * dx, isum, acc) (dw * dx is exact in fp32 and the product exact in
 // fp64, so each block adds with one rounding), columns go two at a time (a
 // last odd column alone) and the wave's row sums are reduced together.
+//
+// Row-scaled int4 / int2 experts (the row-scaled codec) take the same path:
+// no per-block weight scale (a block sum is dx * isum, in fp64), and the
+// row's fp32 scale multiplies the row's total once, after the reduction;
+// int2 blocks are 8 bytes with the -2 offset.
 #include "internal.h"
 #include "qdot.h"
 
@@ -38,10 +43,11 @@ constexpr size_t XLDS = 40 * 1024;    // LDS budget of the staged columns per wo
 
 // EPI_SWIGLU: units are (gate row f, up row ffn + f), output y[col][f];
 // EPI_STORE: units are rows, output y[col][row].  U blocks per lane and row
-// (K <= 64 U blocks), UPW units per wave and row group.
+// (K <= 64 U blocks), UPW units per wave and row group.  FMT: FMT_Q4_0
+// (fp16 scale per block) or FMT_Q4_ROW / FMT_Q2_ROW (fp32 scale per row).
 // Register budget: two workgroups per CU; the one-block down rows (128
 // VGPRs) four.
-template <int EPI, int U, int UPW>
+template <int FMT, int EPI, int U, int UPW>
 __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_expert_gemv(const GemvArgs a,
                                                                                             int mcols) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -61,11 +67,14 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
     const int n_it = (int)((units + PER_IT - 1) / PER_IT);
     if ((int)blockIdx.x >= n_it) return;
 
-    const uint32_t k = (uint32_t)a.k, nb = k / QBLK, rowb = nb * 16u;
+    constexpr uint32_t BB = FMT == FMT_Q2_ROW ? 8u : 16u;   // weight bytes per block
+    constexpr int OFF = FMT == FMT_Q2_ROW ? -2 : -8;          // code offset of the weights
+    const uint32_t k = (uint32_t)a.k, nb = k / QBLK, rowb = nb * BB;
     const uint8_t* __restrict__ wq = a.wq + (int64_t)g * a.wq_gstride;
-    const uint16_t* __restrict__ wd = a.wd + (int64_t)g * a.wd_gstride;
+    const uint16_t* __restrict__ wd = FMT == FMT_Q4_0 ? a.wd + (int64_t)g * a.wd_gstride : nullptr;
+    const float* __restrict__ wr = FMT != FMT_Q4_0 ? a.wr + (int64_t)g * a.wr_gstride : nullptr;
     // LDS: codes [mcols][k], then per (column, block) the fp32 scale's bits
-    // and -8 * the block's code sum
+    // and OFF * the block's code sum
     int8_t* lxq = reinterpret_cast<int8_t*>(smem);
     int2* lsx = reinterpret_cast<int2*>(smem + (size_t)mcols * k);
     const int64_t ffn = a.ffn;
@@ -83,6 +92,7 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
     // (its half picked where it is used): 16-bit loads let the compiler pack
     // two scales into one register as they arrive, which waits on them, and
     // so on every load before them, in the middle of the next group's loads.
+    // Row-scaled weights keep the row's fp32 scale in d[j][0].
     auto load = [&](uint4 (&w)[R][U], uint32_t (&d)[R][U], int it) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -92,9 +102,17 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
             for (int u = 0; u < U; ++u) {
                 uint32_t b = (uint32_t)(u * WAVE + lane);
                 b = b < nb ? b : 0u;
-                w[j][u] = load_stream16(wq + (row * rowb + b * 16u));
-                d[j][u] = *reinterpret_cast<const uint32_t*>(
-                    reinterpret_cast<const char*>(wd) + (((row * nb + b) * 2u) & ~3u));
+                if (FMT == FMT_Q2_ROW) {
+                    const uint2 v = load_stream8(wq + (row * rowb + b * BB));
+                    w[j][u] = make_uint4(v.x, v.y, 0u, 0u);
+                } else {
+                    w[j][u] = load_stream16(wq + (row * rowb + b * BB));
+                }
+                if (FMT == FMT_Q4_0)
+                    d[j][u] = *reinterpret_cast<const uint32_t*>(
+                        reinterpret_cast<const char*>(wd) + (((row * nb + b) * 2u) & ~3u));
+                else if (u == 0)
+                    d[j][0] = __builtin_bit_cast(uint32_t, wr[row]);
             }
         }
     };
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
             const float dx = h2f(a.xd[row * (int64_t)nb + b]);
             *reinterpret_cast<uint4*>(lxq + (size_t)m * k + b * QBLK) = x0;
             *reinterpret_cast<uint4*>(lxq + (size_t)m * k + b * QBLK + 16) = x1;
-            lsx[(size_t)m * nb + b] = make_int2(__builtin_bit_cast(int, dx), -8 * byte_sum(x0, x1));
+            lsx[(size_t)m * nb + b] = make_int2(__builtin_bit_cast(int, dx), OFF * byte_sum(x0, x1));
         }
     };
 
@@ -146,8 +164,14 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
                 const float dx = __builtin_bit_cast(float, sx.x);
 #pragma unroll
                 for (int j = 0; j < R; ++j) {
-                    const int sdot = dot_block(w[j][u], x0, x1, sx.y);
-                    acc[j][m] = fma((double)(scale(d, it, j, u) * dx), (double)sdot, acc[j][m]);
+                    if (FMT == FMT_Q4_0) {
+                        const int sdot = dot_block(w[j][u], x0, x1, sx.y);
+                        acc[j][m] = fma((double)(scale(d, it, j, u) * dx), (double)sdot, acc[j][m]);
+                    } else {
+                        const int sdot = FMT == FMT_Q2_ROW ? dot_block2(w[j][u], x0, x1, sx.y)
+                                                           : dot_block(w[j][u], x0, x1, sx.y);
+                        acc[j][m] = fma((double)dx, (double)sdot, acc[j][m]);
+                    }
                 }
             }
         }
@@ -178,6 +202,16 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
         }
         const int r = base + kk;
         const int m = r / R, j = r % R;
+        if (FMT != FMT_Q4_0) {   // the row scales, applied once to the row totals
+            float d1 = __builtin_bit_cast(float, d[0][0]), d2 = d1;
+#pragma unroll
+            for (int q = 1; q < R; ++q) {
+                if (j == q) d1 = __builtin_bit_cast(float, d[q][0]);
+                if ((j ^ 1) == q) d2 = __builtin_bit_cast(float, d[q][0]);
+            }
+            s *= (double)d1;
+            if (P == 2) s2 *= (double)d2;
+        }
         const int64_t pr = prow(it, j);
         constexpr int OWN = NN >= 4 ? 16 : 32;   // lanes holding one sum
         const bool owner = (NV > 1 ? kk < NV : (lane & (OWN - 1)) == 0) && pr >= 0;
@@ -229,29 +263,42 @@ __global__ __launch_bounds__(256, (U == 1 && EPI == EPI_STORE) ? 4 : 2) void k_e
     }
 }
 
-template <int EPI, int U, int UPW>
+template <int FMT, int EPI, int U, int UPW>
 void launch_x(const GemvArgs& a, int mcols, size_t lds, hipStream_t s) {
     const int64_t units = EPI == EPI_SWIGLU ? a.ffn : a.n;
     const int64_t n_it = (units + 4 * UPW - 1) / (4 * UPW);
     dim3 grid((unsigned)std::min<int64_t>(n_it, XWG), (unsigned)a.groups);
-    hipLaunchKernelGGL((k_expert_gemv<EPI, U, UPW>), grid, dim3(256), lds, s, a, mcols);
+    hipLaunchKernelGGL((k_expert_gemv<FMT, EPI, U, UPW>), grid, dim3(256), lds, s, a, mcols);
+}
+
+template <int FMT>
+void launch_f(const GemvArgs& a, int epi, int64_t nb, int mcols, size_t lds, hipStream_t s) {
+    if (epi == EPI_SWIGLU) {
+        if (nb <= WAVE) launch_x<FMT, EPI_SWIGLU, 1, 2>(a, mcols, lds, s);
+        else launch_x<FMT, EPI_SWIGLU, 3, 1>(a, mcols, lds, s);
+    } else {
+        if (nb <= WAVE) launch_x<FMT, EPI_STORE, 1, 4>(a, mcols, lds, s);
+        else launch_x<FMT, EPI_STORE, 3, 2>(a, mcols, lds, s);
+    }
 }
 
 }  // namespace
 
-// The scales are read as aligned 32-bit words: the array must be 4-byte
+// Q4_0 scales are read as aligned 32-bit words: the array must be 4-byte
 // aligned and each expert's scale count even, so that the word holding an
 // expert's last scale lies inside the expert's scales.
 bool expert_gemv_fits(const GemvArgs& a) {
     const int64_t nb = a.k / QBLK;
-    return a.fmt == FMT_Q4_0 && a.col_off && !a.residual && a.k % QBLK == 0 && nb >= 1 &&
-           nb <= 3 * WAVE && a.wd && QK_ALIGNED(a.wd, 4) && a.wd_gstride % 2 == 0 &&
-           QK_ALIGNED(a.xq, 16);
+    const bool scales = a.fmt == FMT_Q4_0 ? (a.wd && QK_ALIGNED(a.wd, 4) && a.wd_gstride % 2 == 0)
+                                          : (a.fmt == FMT_Q4_ROW || a.fmt == FMT_Q2_ROW) && a.wr &&
+                                                QK_ALIGNED(a.wr, 4);
+    return scales && a.col_off && !a.residual && a.k % QBLK == 0 && nb >= 1 && nb <= 3 * WAVE &&
+           QK_ALIGNED(a.xq, 16) && QK_ALIGNED(a.wq, a.fmt == FMT_Q2_ROW ? 8 : 16);
 }
 
 int launch_expert_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     if (!expert_gemv_fits(a) || (epi != EPI_SWIGLU && epi != EPI_STORE)) return QK_ESHAPE;
-    // one expert's matrix below 4 GiB of nibbles (32-bit offsets in the kernel)
+    // one expert's matrix below 4 GiB of weight bytes (32-bit offsets in the kernel)
     const uint64_t rows = epi == EPI_SWIGLU ? 2 * (uint64_t)a.ffn : (uint64_t)a.n;
     if (rows * (uint64_t)(a.k / 2) >= (1ull << 32)) return QK_ESHAPE;
     if (a.groups <= 0) return QK_OK;
@@ -260,13 +307,9 @@ int launch_expert_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     const int mcols = (int)std::min<size_t>(16, XLDS / per_col);
     if (mcols < 1) return QK_ESHAPE;
     const size_t lds = (size_t)mcols * per_col;
-    if (epi == EPI_SWIGLU) {
-        if (nb <= WAVE) launch_x<EPI_SWIGLU, 1, 2>(a, mcols, lds, s);
-        else launch_x<EPI_SWIGLU, 3, 1>(a, mcols, lds, s);
-    } else {
-        if (nb <= WAVE) launch_x<EPI_STORE, 1, 4>(a, mcols, lds, s);
-        else launch_x<EPI_STORE, 3, 2>(a, mcols, lds, s);
-    }
+    if (a.fmt == FMT_Q4_0) launch_f<FMT_Q4_0>(a, epi, nb, mcols, lds, s);
+    else if (a.fmt == FMT_Q4_ROW) launch_f<FMT_Q4_ROW>(a, epi, nb, mcols, lds, s);
+    else launch_f<FMT_Q2_ROW>(a, epi, nb, mcols, lds, s);
     return qk_launch_status();
 }
 

@@ -26,33 +26,6 @@
 
 namespace qk {
 
-namespace {
-
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
-    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
-    return make_uint2(v.x, v.y);
-}
-
-// Row-scaled int2 block (8 bytes in w.x, w.y): byte j holds elements j, j + 8,
-// j + 16, j + 24 in bits 0-1, 2-3, 4-5, 6-7, so shifting the two words by 0,
-// 2, 4, 6 and masking gives elements 0-7, 8-15, 16-23, 24-31 in order.
-__device__ __forceinline__ int dot_block2(const uint4 w, const uint4 x0, const uint4 x1, int s) {
-    const uint32_t m2 = 0x03030303u;
-    s = __builtin_amdgcn_sdot4((int)(w.x & m2), (int)x0.x, s, false);
-    s = __builtin_amdgcn_sdot4((int)(w.y & m2), (int)x0.y, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.x >> 2) & m2), (int)x0.z, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.y >> 2) & m2), (int)x0.w, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.x >> 4) & m2), (int)x1.x, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.y >> 4) & m2), (int)x1.y, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.x >> 6) & m2), (int)x1.z, s, false);
-    s = __builtin_amdgcn_sdot4((int)((w.y >> 6) & m2), (int)x1.w, s, false);
-    return s;
-}
-
-}  // namespace
-
 // Workgroup-wide RMSNorm / Q8_0 of one activation row into LDS.  Each lane
 // takes 8 consecutive values per 2048-value chunk (four lanes per Q8_0 block),
 // with the same arithmetic as the standalone quantizer.  `load_row` loads

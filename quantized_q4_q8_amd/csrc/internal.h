@@ -91,8 +91,9 @@ int64_t gemv_argmax_parts(int64_t n, int64_t k, int64_t max_cols);
 int launch_quantize_q8(const float* x, int64_t rows, int64_t k, int8_t* xq, uint16_t* xd,
                        hipStream_t s);
 
-// Grouped expert GEMV of the MoE layer (Q4_0, col_off set, no residual,
-// K <= 6144, EPI_SWIGLU or EPI_STORE): each workgroup stages one group's
+// Grouped expert GEMV of the MoE layer (Q4_0 or row-scaled int4 / int2,
+// col_off set, no residual, K <= 6144, EPI_SWIGLU or EPI_STORE): each
+// workgroup stages one group's
 // columns once and walks a share of its rows with the next rows' weight
 // loads in flight.  Returns QK_ESHAPE for arguments outside that
 // (expert_gemv_fits tells beforehand).

@@ -1,7 +1,8 @@
-// Device helpers of the Q4_0 x Q8_0 block dot shared by the GEMV kernels and
-// the persistent decode kernel: the integer block dot of one 32-block, the
-// byte sum that applies the -8 nibble offset, the SwiGLU of two matmul
-// outputs, the streaming weight load and the all-rows wave reduction.
+// Device helpers of the Q4_0 x Q8_0 block dot shared by the GEMV kernels, the
+// expert GEMV and the persistent decode kernel: the integer block dot of one
+// 32-block (and of a row-scaled int2 block), the byte sum that applies the
+// nibble offset, the SwiGLU of two matmul outputs, the streaming weight loads
+// and the all-rows wave reduction.
 // The product is the block form of kenji.blog's llama.cpp guide, section 2.2.
 #pragma once
 
@@ -42,6 +43,22 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
     return (float)(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
+// Row-scaled int2 block (8 bytes in w.x, w.y): byte j holds elements j, j + 8,
+// j + 16, j + 24 in bits 0-1, 2-3, 4-5, 6-7, so shifting the two words by 0,
+// 2, 4, 6 and masking gives elements 0-7, 8-15, 16-23, 24-31 in order.
+__device__ __forceinline__ int dot_block2(const uint4 w, const uint4 x0, const uint4 x1, int s) {
+    const uint32_t m2 = 0x03030303u;
+    s = __builtin_amdgcn_sdot4((int)(w.x & m2), (int)x0.x, s, false);
+    s = __builtin_amdgcn_sdot4((int)(w.y & m2), (int)x0.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 2) & m2), (int)x0.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 2) & m2), (int)x0.w, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 4) & m2), (int)x1.x, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 4) & m2), (int)x1.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.x >> 6) & m2), (int)x1.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)((w.y >> 6) & m2), (int)x1.w, s, false);
+    return s;
+}
+
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // 16-byte weight load marked non-temporal: weights stream through once per
@@ -49,6 +66,14 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
     const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// The same for an 8-byte block (row-scaled int2).
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(v.x, v.y);
 }
 
 
