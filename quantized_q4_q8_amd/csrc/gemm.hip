@@ -212,7 +212,10 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     for (int64_t s = 0; s < nsteps; ++s) {
         Stage& cur = st[s & 1];
         if (s + 1 < nsteps) gload((s + 1) * KB);
-#pragma unroll 1
+        // two blocks per iteration: the second one's LDS addresses become
+        // immediate offsets (1.9 % on the 4 x 512 prefill; a full unroll of
+        // the four spills)
+#pragma unroll 2
         for (int bb = 0; bb < KB; ++bb) {
             const uint4 av = *reinterpret_cast<const uint4*>(cur.a + tra * STRIDE + bb * QBLK + h * 16);
             const v4i xa = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
