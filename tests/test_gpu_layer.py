@@ -296,7 +296,11 @@ def moe_expected(sel_g, w_g, sel_o, out_o, logits, expert_y):
 @pytest.mark.parametrize("T,H,E,F,k", [(8, 256, 16, 64, 4), (33, 512, 64, 96, 8), (1, 128, 8, 32, 1),
                                        # 1600 pairs: the grouping's second chunk of 1024,
                                        # about 100 tokens per expert (passes of 8 columns)
-                                       (200, 64, 16, 32, 8)])
+                                       (200, 64, 16, 32, 8),
+                                       # gate/up rows of 256 blocks: past the expert GEMV's
+                                       # 192, so the grouped GEMV's multi-step rows take them;
+                                       # the down projection stays on the expert GEMV
+                                       (6, 8192, 8, 64, 2)])
 def test_moe_matches_oracle(gpu_lib, T, H, E, F, k):
     qk = gpu_lib
     say(f"moe_route_and_apply T={T} H={H} E={E} F={F} k={k}")
