@@ -37,6 +37,82 @@ size_t attention_ws_bytes(int64_t tokens, int64_t nq, int64_t nkv, int64_t hd, i
     return align256((size_t)(tokens * nq * nch * (hd + 2)) * sizeof(double));
 }
 
+// One thread's 8-value piece of a K and a V row (fp16 bits) into the
+// chunk's LDS rows as fp32 (exact widenings).
+template <int HD>
+__device__ __forceinline__ void stage_kv_piece(const uint4 kv, const uint4 vv, int r, int d,
+                                               float (*ks)[HD + 4], float (*vs)[HD]) {
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    float4 k0, k1, v0, v1;
+    k0.x = h2f((uint16_t)(kw[0] & 0xFFFF)); k0.y = h2f((uint16_t)(kw[0] >> 16));
+    k0.z = h2f((uint16_t)(kw[1] & 0xFFFF)); k0.w = h2f((uint16_t)(kw[1] >> 16));
+    k1.x = h2f((uint16_t)(kw[2] & 0xFFFF)); k1.y = h2f((uint16_t)(kw[2] >> 16));
+    k1.z = h2f((uint16_t)(kw[3] & 0xFFFF)); k1.w = h2f((uint16_t)(kw[3] >> 16));
+    v0.x = h2f((uint16_t)(vw[0] & 0xFFFF)); v0.y = h2f((uint16_t)(vw[0] >> 16));
+    v0.z = h2f((uint16_t)(vw[1] & 0xFFFF)); v0.w = h2f((uint16_t)(vw[1] >> 16));
+    v1.x = h2f((uint16_t)(vw[2] & 0xFFFF)); v1.y = h2f((uint16_t)(vw[2] >> 16));
+    v1.z = h2f((uint16_t)(vw[3] & 0xFFFF)); v1.w = h2f((uint16_t)(vw[3] >> 16));
+    *reinterpret_cast<float4*>(&ks[r][d]) = k0;
+    *reinterpret_cast<float4*>(&ks[r][d + 4]) = k1;
+    *reinterpret_cast<float4*>(&vs[r][d]) = v0;
+    *reinterpret_cast<float4*>(&vs[r][d + 4]) = v1;
+}
+
+// One query head against the chunk's first `rows` LDS rows (one wave): the
+// chunk max m, the exp-sum l and, in lanes < HD, the un-normalized output of
+// dimension `lane`.  esw is the wave's row of exp weights.
+template <int HD>
+__device__ __forceinline__ void head_chunk(const double* qh, const float (*ks)[HD + 4],
+                                           const float (*vs)[HD], double* esw, int lane, int rows,
+                                           double& m, double& l, double& oc) {
+    const double rscale = sqrt((double)HD);
+    double s = -INFINITY;
+    if (lane < rows) {   // score of row `lane`
+        double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+#pragma unroll
+        for (int d = 0; d < HD; d += 4) {
+            const float4 kk = *reinterpret_cast<const float4*>(&ks[lane][d]);
+            const double2 qa = *reinterpret_cast<const double2*>(&qh[d]);
+            const double2 qb = *reinterpret_cast<const double2*>(&qh[d + 2]);
+            d0 = fma(qa.x, (double)kk.x, d0);
+            d1 = fma(qa.y, (double)kk.y, d1);
+            d2 = fma(qb.x, (double)kk.z, d2);
+            d3 = fma(qb.y, (double)kk.w, d3);
+        }
+        s = ((d0 + d1) + (d2 + d3)) / rscale;
+    }
+    m = group_max<WAVE>(s);
+    const double e = lane < rows ? exp(s - m) : 0.0;
+    l = group_sum<WAVE>(e);
+    esw[lane] = e;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    oc = 0.0;
+    if (lane < HD) {   // weighted values, lane = dimension
+        double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
+        if (rows == ACH) {   // full chunk: unrolled, LDS reads run ahead
+#pragma unroll
+            for (int r = 0; r < ACH; r += 4) {
+                const double2 ea = *reinterpret_cast<const double2*>(&esw[r]);
+                const double2 eb = *reinterpret_cast<const double2*>(&esw[r + 2]);
+                o0 = fma(ea.x, (double)vs[r][lane], o0);
+                o1 = fma(ea.y, (double)vs[r + 1][lane], o1);
+                o2 = fma(eb.x, (double)vs[r + 2][lane], o2);
+                o3 = fma(eb.y, (double)vs[r + 3][lane], o3);
+            }
+        } else {
+            int r = 0;
+            for (; r + 1 < rows; r += 2) {
+                const double2 ee = *reinterpret_cast<const double2*>(&esw[r]);
+                o0 = fma(ee.x, (double)vs[r][lane], o0);
+                o1 = fma(ee.y, (double)vs[r + 1][lane], o1);
+            }
+            if (r < rows) o0 = fma(esw[r], (double)vs[r][lane], o0);
+        }
+        oc = (o0 + o1) + (o2 + o3);
+    }
+}
+
 // Chunk pass.  Workgroup (chunk c, KV head g, token t) reads cache rows
 // [64 c, 64 c + 64) intersected with [0, pos[t]] of its sequence once for all
 // query heads of group g; wave w takes query heads w, w + 8, ...  For its head
@@ -163,8 +239,103 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
     }
 }
 
-// Merge pass: workgroup (head h, token t) combines the head's chunk records
-// by log-sum-exp rescaling, out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+// Chunk pass for long caches: workgroup (record x, KV head g, token t) walks
+// the LCPW chunks from chunk LCPW x on, with the next chunk's rows loaded
+// while the current one is used, and folds them into one record per head by
+// the merge pass's log-sum-exp rescaling (both sides scaled to the larger
+// max, in fp64).  A workgroup then streams its rows instead of loading one
+// chunk and stopping, and the merge reads LCPW times fewer records.  (At
+// 8192 rows and fewer the one-chunk pass is faster: its workgroups already
+// fit the chip in one round.)
+constexpr int LCPW = 4;
+
+template <int HD>
+__global__ __launch_bounds__(512) void k_attn_chunk_long(
+    const float* __restrict__ q, int64_t q_ts, int64_t nq, int64_t nkv,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int64_t cap,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, double* __restrict__ rec,
+    int64_t nrec) {
+    constexpr int MAXG = 512 / HD;
+    constexpr int KS = HD + 4;
+    constexpr int NW = 8;
+    constexpr int HPW = (MAXG + NW - 1) / NW;   // query heads per wave, at most
+    __shared__ __align__(16) double qs[MAXG][HD];
+    __shared__ __align__(16) float ks[ACH][KS];
+    __shared__ __align__(16) float vs[ACH][HD];
+    __shared__ __align__(16) double es[NW][ACH];
+
+    const int64_t x = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+    const int G = (int)(nq / nkv);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int p = pos[t];
+    const int sq = seq[t];
+    asm volatile("" ::"s"(p), "s"(sq));
+    if (p < 0) return;
+    const int64_t pe = min((int64_t)p, cap - 1);
+    const int64_t c0 = x * LCPW;
+    if (c0 * ACH > pe) return;
+    const int nc = (int)min((int64_t)LCPW, pe / ACH - c0 + 1);   // chunks with rows
+
+    static_assert(ACH * HD / 8 <= 512, "one K/V piece per thread");
+    const int iq = tid < G * HD ? tid : 0;
+    const float qv = q[t * q_ts + (g * G) * HD + iq];
+    const int64_t hbase = ((int64_t)sq * nkv + g) * cap * HD;
+    const int i = tid < ACH * HD / 8 ? tid : 0;
+    const int r = (i * 8) / HD, d = (i * 8) % HD;
+    uint4 kv, vv;
+    auto load_kv = [&](int64_t c) {   // clamped into the chunk's rows
+        const int rows = (int)min((int64_t)ACH, pe + 1 - c * ACH);
+        const int64_t roff = (c * ACH + (r < rows ? r : 0)) * HD + d;
+        kv = *reinterpret_cast<const uint4*>(kc + hbase + roff);
+        vv = *reinterpret_cast<const uint4*>(vc + hbase + roff);
+    };
+    load_kv(c0);
+    if (tid < G * HD) qs[tid / HD][tid % HD] = (double)qv;
+
+    double rm[HPW], rl[HPW], ro[HPW];
+    for (int j = 0; j < nc; ++j) {
+        const int64_t c = c0 + j;
+        const int rows = (int)min((int64_t)ACH, pe + 1 - c * ACH);
+        if (j > 0) __syncthreads();   // every wave is done with the previous chunk's rows
+        if (tid < ACH * HD / 8) stage_kv_piece<HD>(kv, vv, r, d, ks, vs);
+        __syncthreads();
+        if (j + 1 < nc) load_kv(c + 1);
+#pragma unroll
+        for (int hi = 0; hi < HPW; ++hi) {
+            const int hh = wave + hi * NW;
+            if (hh >= G) break;
+            double m, l, oc;
+            head_chunk<HD>(qs[hh], ks, vs, es[wave], lane, rows, m, l, oc);
+            if (j == 0) {
+                rm[hi] = m;
+                rl[hi] = l;
+                ro[hi] = oc;
+            } else {
+                const double mn = fmax(rm[hi], m);
+                const double a = exp(rm[hi] - mn), b = exp(m - mn);
+                rl[hi] = rl[hi] * a + l * b;
+                ro[hi] = ro[hi] * a + oc * b;
+                rm[hi] = mn;
+            }
+            __builtin_amdgcn_wave_barrier();   // es is rewritten for the next head
+        }
+    }
+#pragma unroll
+    for (int hi = 0; hi < HPW; ++hi) {
+        const int hh = wave + hi * NW;
+        if (hh >= G) break;
+        double* rp = rec + ((t * nq + g * G + hh) * nrec + x) * (HD + 2);
+        if (lane < HD) rp[2 + lane] = ro[hi];
+        if (lane == 0) {
+            rp[0] = rm[hi];
+            rp[1] = rl[hi];
+        }
+    }
+}
+
+// Merge pass: workgroup (head h, token t) combines the head's nch records
+// (one per 2^CPW_LOG2 chunks) by log-sum-exp rescaling,
+// out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Thread (pair i, slice s) owns output dimensions 2i, 2i + 1 over chunks
 // s, s + SLICES, ...; threads c and c + 256 load chunk c's and chunk
 // c + 256's (m, l).  The (m, l) loads and a thread's first PB output pairs
@@ -175,7 +346,7 @@ __global__ __launch_bounds__(512) void k_attn_chunk(
 // and/or its Q8_0 codes (four lanes per block).  SPLIT > 1 (long contexts):
 // the head's dims are split over SPLIT workgroups (grid z), each a whole
 // number of Q8_0 blocks; every split forms the same chunk weights.
-template <int HD, int SPLIT>
+template <int HD, int SPLIT, int CPW_LOG2 = 0>
 __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ rec, int64_t nq,
                                                     int64_t nch, int64_t cap,
                                                     const int32_t* __restrict__ pos,
@@ -198,7 +369,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     const int p = pos[t];
     const int64_t col = h * HD + d0;
     const bool valid = p >= 0;   // negative position: zeros, no reads
-    const int used = valid ? (int)(min((int64_t)p, cap - 1) / ACH) + 1 : 0;
+    const int used = valid ? (int)((min((int64_t)p, cap - 1) / ACH) >> CPW_LOG2) + 1 : 0;   // records with rows
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
     const int pr = tid % PAIRS, sl = tid / PAIRS;
 
@@ -622,22 +793,47 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
         return qk_launch_status();
     }
     double* rec = static_cast<double*>(ws);
-    dim3 grid((unsigned)nch, (unsigned)nkv, (unsigned)tokens);
+    // caches of 256 chunks or more (16384 rows): LCPW chunks per chunk-pass
+    // workgroup, one record for them
+    static_assert(LCPW == 4, "the merge's CPW_LOG2 below");
+    const bool lng = nch >= 256;
+    const int64_t nrec = lng ? (nch + LCPW - 1) / LCPW : nch;   // records per head
+    dim3 grid((unsigned)nrec, (unsigned)nkv, (unsigned)tokens);
     dim3 mgrid((unsigned)nq, (unsigned)tokens);
+    dim3 mgrid2((unsigned)nq, (unsigned)tokens, 2u);
     if (hd == 32) {
-        hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
-                           pos, seq, rec, nch);
-        hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
-                           o_ts, oq, od);
-    } else if (hd == 64) {
-        hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
-                           pos, seq, rec, nch);
-        if (nch > 64)   // long contexts: two workgroups per head, 32 dims each
-            hipLaunchKernelGGL((k_attn_merge<64, 2>), dim3((unsigned)nq, (unsigned)tokens, 2u), dim3(256), 0,
-                               s, rec, nq, nch, cap, pos, out, o_ts, oq, od);
-        else
-            hipLaunchKernelGGL((k_attn_merge<64, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
+        if (lng) {
+            hipLaunchKernelGGL(k_attn_chunk_long<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc,
+                               cap, pos, seq, rec, nrec);
+            hipLaunchKernelGGL((k_attn_merge<32, 1, 2>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                               out, o_ts, oq, od);
+        } else {
+            hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
+                               pos, seq, rec, nch);
+            hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
                                o_ts, oq, od);
+        }
+    } else if (hd == 64) {
+        if (lng) {
+            hipLaunchKernelGGL(k_attn_chunk_long<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc,
+                               cap, pos, seq, rec, nrec);
+            // many records (more than 64): two workgroups per head, 32 dims each
+            if (nrec > 64)
+                hipLaunchKernelGGL((k_attn_merge<64, 2, 2>), mgrid2, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                                   out, o_ts, oq, od);
+            else
+                hipLaunchKernelGGL((k_attn_merge<64, 1, 2>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                                   out, o_ts, oq, od);
+        } else {
+            hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
+                               pos, seq, rec, nch);
+            if (nch > 64)   // long contexts: two workgroups per head, 32 dims each
+                hipLaunchKernelGGL((k_attn_merge<64, 2>), mgrid2, dim3(256), 0, s, rec, nq, nch, cap, pos,
+                                   out, o_ts, oq, od);
+            else
+                hipLaunchKernelGGL((k_attn_merge<64, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos,
+                                   out, o_ts, oq, od);
+        }
     } else {
         return QK_ESHAPE;
     }

@@ -327,6 +327,12 @@ ATT_CASES = [
     (2, 32, 4, 64, 32768, 2, "ring"),
     (2, 16, 2, 32, 32768, 2, "ring"),
     (40, 32, 4, 64, 16384, 1, "long9k"),  # many tokens past 8192: the tiled pass
+    # caches of 256 chunks and more: four chunks per chunk-pass workgroup and
+    # record; positions at chunk and four-chunk boundaries give records of
+    # one to four chunks and workgroups with nothing to read
+    (8, 32, 4, 64, 32768, 8, "spread"),
+    (3, 32, 4, 64, 16384, 3, "spread"),
+    (8, 16, 2, 32, 32768, 8, "spread"),
     # head groups that do not divide the 64 query rows of a tiled-pass workgroup
     (24, 12, 4, 64, 100, 2, "random"),    # G = 3: 21 tokens x 3 heads per workgroup
     (25, 24, 4, 32, 90, 1, "prefill"),    # G = 6, head_dim 32
@@ -354,6 +360,8 @@ def test_gqa_attention(gpu_lib, tokens, nq, nkv, hd, cap, seqs, recipe):
         pos = (2100 + np.arange(tokens)).astype(np.int32)
     elif recipe == "long9k":
         pos = (9000 + np.arange(tokens)).astype(np.int32)
+    elif recipe == "spread":
+        pos = np.array([cap // 2 - 1, 255, cap - 700, 0, 63, 64, 256, 5000], np.int32)[:tokens]
     elif recipe == "ring":
         pos = np.array([cap - 1, cap, 2 * cap + 37, 5 * cap + 3] * 3, np.int32)[:tokens] + \
             (synth.randint(111, 5, tokens, 7)).astype(np.int32)
