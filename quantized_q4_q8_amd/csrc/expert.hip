@@ -285,11 +285,13 @@ void launch_f(const GemvArgs& a, int epi, int64_t nb, int mcols, size_t lds, hip
 }  // namespace
 
 // Q4_0 scales are read as aligned 32-bit words: the array must be 4-byte
-// aligned and each expert's scale count even, so that the word holding an
-// expert's last scale lies inside the expert's scales.
+// aligned, each expert's scales must start on a word (even stride) and their
+// count (n rows of nb blocks) be even, so that the word holding an expert's
+// last scale lies inside the expert's scales.
 bool expert_gemv_fits(const GemvArgs& a) {
     const int64_t nb = a.k / QBLK;
-    const bool scales = a.fmt == FMT_Q4_0 ? (a.wd && QK_ALIGNED(a.wd, 4) && a.wd_gstride % 2 == 0)
+    const bool scales = a.fmt == FMT_Q4_0 ? (a.wd && QK_ALIGNED(a.wd, 4) && a.wd_gstride % 2 == 0 &&
+                                             (a.n * nb) % 2 == 0)
                                           : (a.fmt == FMT_Q4_ROW || a.fmt == FMT_Q2_ROW) && a.wr &&
                                                 QK_ALIGNED(a.wr, 4);
     return scales && a.col_off && !a.residual && a.k % QBLK == 0 && nb >= 1 && nb <= 3 * WAVE &&
