@@ -280,6 +280,41 @@ def test_kv_append_bit_exact(gpu_lib):
     assert np.array_equal(host(vcg, np.uint16), vc)
 
 
+@pytest.mark.parametrize("tokens", [6, 13])
+def test_negative_positions_read_and_write_nothing(gpu_lib, tokens):
+    """Negative positions (padding tokens) as the header states them: the KV
+    store skips their rows and attention gives them zero rows, on the
+    few-token chunk/merge pass (6 tokens) and on the tiled pass (13).  The
+    other tokens equal the oracle over them alone (the oracle takes
+    non-negative positions only; a token's result depends on its own
+    position, sequence and query and on the cache)."""
+    qk = gpu_lib
+    say(f"negative positions, {tokens} tokens")
+    nq, nkv, hd, cap, seqs = 8, 2, 64, 300, 2
+    neg = np.arange(tokens) % 3 == 1
+    pos = synth.randint(112, 4, tokens, cap).astype(np.int32)
+    pos[neg] = -1 - 37 * np.arange(int(neg.sum()), dtype=np.int32)   # -1, -38, ...
+    seq = (np.arange(tokens) % seqs).astype(np.int32)
+    # KV store: one token per (sequence, position) so that the result does
+    # not depend on the order of the stores
+    k = synth.normal(112, 5, (tokens, nkv, hd))
+    v = synth.normal(112, 6, (tokens, nkv, hd))
+    kpos = np.where(neg, pos, np.arange(tokens, dtype=np.int32) * 7)
+    kc, vc = _cache(112, seqs, nkv, cap, hd, cap // 2)
+    kcg, vcg = dev(kc), dev(vc)
+    qk.qk_kv_append(dev(k), dev(v), dev(kpos), dev(seq), kcg, vcg)
+    oracle.kv_append(k[~neg], v[~neg], kpos[~neg], seq[~neg], kc, vc)
+    assert np.array_equal(host(kcg, np.uint16), kc)
+    assert np.array_equal(host(vcg, np.uint16), vc)
+    # attention over the updated caches
+    q = synth.normal(112, 3, (tokens, nq, hd))
+    out = host(qk.gqa_attention(dev(q), kcg, vcg, dev(pos), dev(seq)))
+    assert np.all(out[neg] == 0.0)
+    ref = oracle.gqa_attention(q[~neg], kc, vc, pos[~neg], seq[~neg])
+    assert rel_err(out[~neg], ref) < 1e-5
+    assert_same_fp32(out[~neg], ref)
+
+
 def test_embed_and_argmax(gpu_lib):
     qk = gpu_lib
     say("qk_embed_lookup, qk_argmax")
