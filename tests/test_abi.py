@@ -130,3 +130,38 @@ def test_decode_greedy_validation_host_only(lib):
     flag = ctypes.c_int32(7)
     assert lib.qk_decode_error(None, ctypes.byref(cfg), ctypes.byref(flag)) == qk.QK_EINVAL
     assert flag.value == 7
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "qk.h"
+
+int main(void) {
+    qk_layer_cfg cfg = {2048, 32, 4, 64, 5632, 1e-5f, 10000.0f, 2176};
+    size_t one = qk_layer_workspace(&cfg, 1), many = qk_layer_workspace(&cfg, 512);
+    size_t att = qk_gqa_attention_workspace(4, 32, 64, 2176);
+    printf("%s|%s|%d|%d\n", qk_strerror(QK_OK), qk_strerror(QK_ESHAPE),
+           one > 0 && one <= many, att > 0);
+    return 0;
+}
+"""
+
+
+def test_header_is_c_and_links_from_c(lib, tmp_path):
+    """The header is plain C: a C11 program (pedantic, warnings as errors)
+    includes it, links libqk.so and calls its host-only entry points."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if not gcc:
+        pytest.skip("gcc not available")
+    src, exe = tmp_path / "abi.c", tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    libdir = os.path.dirname(qk.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-lqk", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True, timeout=60).stdout
+    ok, eshape, ws_ok, att_ok = out.strip().split("|")
+    assert ok == lib.qk_strerror(qk.QK_OK).decode() and eshape == lib.qk_strerror(qk.QK_ESHAPE).decode()
+    assert ws_ok == "1" and att_ok == "1"
