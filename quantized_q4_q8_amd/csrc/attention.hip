@@ -26,6 +26,7 @@ namespace {
 constexpr int ACH = 64;            // cache rows per chunk: one per lane
 constexpr int MAX_CHUNKS = 512;    // chunks per head (cap <= 32768)
 constexpr int64_t FLASH_MIN_TOKENS = 8;   // more tokens than this: the tiled pass
+constexpr int MERGE_W_CHUNKS = 64;         // chunks per head up to which the merge is one wave
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -441,6 +442,71 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     }
 }
 
+// Merge pass in one wave per (head, token), for caches of at most 64 chunks
+// (4096 rows): the same log-sum-exp combination as k_attn_merge with no
+// workgroup barrier.  Lane c loads chunk c's (m, l) and lane d dim d of
+// every record (chunk indexes clamped to chunk 0; the weight of a chunk
+// without rows is 0), the max, the chunk weights and their l-weighted sum
+// are wave reductions, the weights pass through LDS within the wave, and
+// each lane adds its dim's weighted values in chunk order, so the result
+// does not depend on timing.  Head dim 32: lanes 32..63 repeat lanes 0..31
+// and store nothing.  The Q8_0 output goes through LDS to eight values per
+// lane, as in k_attn_merge.
+template <int HD>
+__global__ __launch_bounds__(64) void k_attn_merge_w(const double* __restrict__ rec, int64_t nq,
+                                                     int64_t nch, int64_t cap,
+                                                     const int32_t* __restrict__ pos,
+                                                     float* __restrict__ out, int64_t o_ts,
+                                                     int8_t* __restrict__ oq,
+                                                     uint16_t* __restrict__ od) {
+    static_assert(HD == 32 || HD == 64, "a dim per lane");
+    static_assert(MERGE_W_CHUNKS == WAVE, "a chunk per lane");
+    __shared__ __align__(16) double ws[WAVE];
+    __shared__ __align__(16) float res[HD];
+    const int64_t h = blockIdx.x, t = blockIdx.y;
+    const int lane = threadIdx.x, d = lane & (HD - 1);
+    const int p = pos[t];
+    const bool valid = p >= 0;   // negative position: zeros (its records are not read as results)
+    const int used = valid ? (int)(min((int64_t)p, cap - 1) / ACH) + 1 : 0;   // records with rows
+    const double* hr = rec + (t * nq + h) * nch * (HD + 2);
+    const double2 ml = *reinterpret_cast<const double2*>(hr + (lane < used ? lane : 0) * (HD + 2));
+    double ov[WAVE];
+#pragma unroll
+    for (int c = 0; c < WAVE; ++c) ov[c] = hr[(c < used ? c : 0) * (HD + 2) + 2 + d];
+    const double mx = group_max<WAVE>(lane < used ? ml.x : -INFINITY);
+    const double w = lane < used ? exp(ml.x - mx) : 0.0;
+    const double ls = group_sum<WAVE>(w * ml.y);
+    ws[lane] = w;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < WAVE; c += 2) {
+        const double2 wc = *reinterpret_cast<const double2*>(&ws[c]);
+        acc = fma(wc.x, ov[c], acc);
+        acc = fma(wc.y, ov[c + 1], acc);
+    }
+    const float v = valid ? (float)(acc / ls) : 0.0f;
+    const int64_t col = t * o_ts + h * HD;
+    if (out && lane < HD) out[col + lane] = v;
+    if (oq) {
+        if (lane < HD) res[lane] = v;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float vv[8];
+        const int i8 = (lane % (HD / 8)) * 8;   // lanes < HD / 8 hold values 8 lane .. 8 lane + 7
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = res[i8 + e];
+        uint32_t lo, hi;
+        float dd;
+        q8_quad(vv, lo, hi, dd);   // four lanes per Q8_0 block
+        if (lane < HD / 8) {
+            *reinterpret_cast<uint2*>(oq + col + 8 * lane) = make_uint2(lo, hi);
+            if ((lane & 3) == 0) od[(col + 8 * lane) / QBLK] = f2h(dd);
+        }
+    }
+}
+
 // Longest-first order of the tiled pass's token tiles (TQ tokens each): a
 // tile's cost is the number of 64-row chunks its furthest position attends,
 // and order[] lists the tiles by cost, largest first (a counting sort; the
@@ -810,8 +876,12 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
         } else {
             hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                                pos, seq, rec, nch);
-            hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos, out,
-                               o_ts, oq, od);
+            if (nch <= MERGE_W_CHUNKS)
+                hipLaunchKernelGGL(k_attn_merge_w<32>, mgrid, dim3(64), 0, s, rec, nq, nch, cap, pos, out,
+                                   o_ts, oq, od);
+            else
+                hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos,
+                                   out, o_ts, oq, od);
         }
     } else if (hd == 64) {
         if (lng) {
@@ -827,12 +897,12 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
         } else {
             hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                                pos, seq, rec, nch);
-            if (nch > 64)   // long contexts: two workgroups per head, 32 dims each
+            if (nch > MERGE_W_CHUNKS)   // long contexts: two workgroups per head, 32 dims each
                 hipLaunchKernelGGL((k_attn_merge<64, 2>), mgrid2, dim3(256), 0, s, rec, nq, nch, cap, pos,
                                    out, o_ts, oq, od);
-            else
-                hipLaunchKernelGGL((k_attn_merge<64, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos,
-                                   out, o_ts, oq, od);
+            else   // up to 64 chunks (the one-wave merge)
+                hipLaunchKernelGGL(k_attn_merge_w<64>, mgrid, dim3(64), 0, s, rec, nq, nch, cap, pos, out,
+                                   o_ts, oq, od);
         }
     } else {
         return QK_ESHAPE;

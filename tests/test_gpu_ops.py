@@ -347,6 +347,7 @@ ATT_CASES = [
     (6, 32, 4, 64, 2176, 3, "ragged"),
     (3, 8, 8, 64, 130, 1, "mha"),
     (2, 16, 1, 32, 70, 2, "mqa"),
+    (6, 16, 2, 32, 4096, 3, "ragged"),    # head_dim 32, 64 chunks: the one-wave merge's limit
     (1, 32, 4, 64, 2176, 1, "first"),
     # many tokens: the tiled pass (runs of one sequence inside 8-token tiles)
     (64, 8, 2, 64, 200, 1, "prefill"),
