@@ -19,6 +19,8 @@
 // once to fp32.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace qk {
 
 namespace {
@@ -26,7 +28,7 @@ namespace {
 constexpr int ACH = 64;            // cache rows per chunk: one per lane
 constexpr int MAX_CHUNKS = 512;    // chunks per head (cap <= 32768)
 constexpr int64_t FLASH_MIN_TOKENS = 8;   // more tokens than this: the tiled pass
-constexpr int MERGE_W_CHUNKS = 64;         // chunks per head up to which the merge is one wave
+constexpr int MERGE_W_CHUNKS = 64;         // records per head up to which the merge is one wave
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -442,17 +444,17 @@ __global__ __launch_bounds__(256) void k_attn_merge(const double* __restrict__ r
     }
 }
 
-// Merge pass in one wave per (head, token), for caches of at most 64 chunks
-// (4096 rows): the same log-sum-exp combination as k_attn_merge with no
-// workgroup barrier.  Lane c loads chunk c's (m, l) and lane d dim d of
-// every record (chunk indexes clamped to chunk 0; the weight of a chunk
-// without rows is 0), the max, the chunk weights and their l-weighted sum
-// are wave reductions, the weights pass through LDS within the wave, and
-// each lane adds its dim's weighted values in chunk order, so the result
-// does not depend on timing.  Head dim 32: lanes 32..63 repeat lanes 0..31
-// and store nothing.  The Q8_0 output goes through LDS to eight values per
-// lane, as in k_attn_merge.
-template <int HD>
+// Merge pass in one wave per (head, token), for at most 64 records per head
+// (each of 2^CPW_LOG2 chunks): the same log-sum-exp combination as
+// k_attn_merge with no workgroup barrier.  Lane c loads record c's (m, l)
+// and lane d dim d of every record (record indexes clamped to record 0; the
+// weight of a record without rows is 0), the max, the record weights and
+// their l-weighted sum are wave reductions, the weights pass through LDS
+// within the wave, and each lane adds its dim's weighted values in record
+// order, so the result does not depend on timing.  Head dim 32: lanes
+// 32..63 repeat lanes 0..31 and store nothing.  The Q8_0 output goes
+// through LDS to eight values per lane, as in k_attn_merge.
+template <int HD, int CPW_LOG2>
 __global__ __launch_bounds__(64) void k_attn_merge_w(const double* __restrict__ rec, int64_t nq,
                                                      int64_t nch, int64_t cap,
                                                      const int32_t* __restrict__ pos,
@@ -460,15 +462,16 @@ __global__ __launch_bounds__(64) void k_attn_merge_w(const double* __restrict__ 
                                                      int8_t* __restrict__ oq,
                                                      uint16_t* __restrict__ od) {
     static_assert(HD == 32 || HD == 64, "a dim per lane");
-    static_assert(MERGE_W_CHUNKS == WAVE, "a chunk per lane");
+    static_assert(MERGE_W_CHUNKS == WAVE, "a record per lane");
     __shared__ __align__(16) double ws[WAVE];
     __shared__ __align__(16) float res[HD];
     const int64_t h = blockIdx.x, t = blockIdx.y;
     const int lane = threadIdx.x, d = lane & (HD - 1);
     const int p = pos[t];
     const bool valid = p >= 0;   // negative position: zeros (its records are not read as results)
-    const int used = valid ? (int)(min((int64_t)p, cap - 1) / ACH) + 1 : 0;   // records with rows
+    const int used = valid ? (int)((min((int64_t)p, cap - 1) / ACH) >> CPW_LOG2) + 1 : 0;   // records with rows
     const double* hr = rec + (t * nq + h) * nch * (HD + 2);
+    // every load is issued before the first wait (one round trip)
     const double2 ml = *reinterpret_cast<const double2*>(hr + (lane < used ? lane : 0) * (HD + 2));
     double ov[WAVE];
 #pragma unroll
@@ -867,42 +870,47 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     dim3 grid((unsigned)nrec, (unsigned)nkv, (unsigned)tokens);
     dim3 mgrid((unsigned)nq, (unsigned)tokens);
     dim3 mgrid2((unsigned)nq, (unsigned)tokens, 2u);
+    // the merge: one wave per head for up to 64 records per head (4096 rows,
+    // or 16384 with the long pass); more records go to k_attn_merge, whose
+    // four waves (two workgroups for head dim 64) load them faster (a
+    // one-wave form with two records per lane measured slower at 8192 and
+    // 32768 rows)
+    auto merge = [&](auto hdc, auto cpw) {
+        constexpr int HD = decltype(hdc)::value, CPW = decltype(cpw)::value;
+        if (nrec <= MERGE_W_CHUNKS) {
+            hipLaunchKernelGGL((k_attn_merge_w<HD, CPW>), mgrid, dim3(64), 0, s, rec, nq, nrec, cap, pos,
+                               out, o_ts, oq, od);
+        } else if constexpr (HD == 64) {   // two workgroups per head, 32 dims each
+            hipLaunchKernelGGL((k_attn_merge<HD, 2, CPW>), mgrid2, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                               out, o_ts, oq, od);
+        } else {
+            hipLaunchKernelGGL((k_attn_merge<HD, 1, CPW>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                               out, o_ts, oq, od);
+        }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C2 = std::integral_constant<int, 2>;
     if (hd == 32) {
+        using H = std::integral_constant<int, 32>;
         if (lng) {
             hipLaunchKernelGGL(k_attn_chunk_long<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc,
                                cap, pos, seq, rec, nrec);
-            hipLaunchKernelGGL((k_attn_merge<32, 1, 2>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
-                               out, o_ts, oq, od);
+            merge(H{}, C2{});
         } else {
             hipLaunchKernelGGL(k_attn_chunk<32>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                                pos, seq, rec, nch);
-            if (nch <= MERGE_W_CHUNKS)
-                hipLaunchKernelGGL(k_attn_merge_w<32>, mgrid, dim3(64), 0, s, rec, nq, nch, cap, pos, out,
-                                   o_ts, oq, od);
-            else
-                hipLaunchKernelGGL((k_attn_merge<32, 1>), mgrid, dim3(256), 0, s, rec, nq, nch, cap, pos,
-                                   out, o_ts, oq, od);
+            merge(H{}, C0{});
         }
     } else if (hd == 64) {
+        using H = std::integral_constant<int, 64>;
         if (lng) {
             hipLaunchKernelGGL(k_attn_chunk_long<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc,
                                cap, pos, seq, rec, nrec);
-            // many records (more than 64): two workgroups per head, 32 dims each
-            if (nrec > 64)
-                hipLaunchKernelGGL((k_attn_merge<64, 2, 2>), mgrid2, dim3(256), 0, s, rec, nq, nrec, cap, pos,
-                                   out, o_ts, oq, od);
-            else
-                hipLaunchKernelGGL((k_attn_merge<64, 1, 2>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
-                                   out, o_ts, oq, od);
+            merge(H{}, C2{});
         } else {
             hipLaunchKernelGGL(k_attn_chunk<64>, grid, dim3(512), 0, s, q, q_ts, nq, nkv, kc, vc, cap,
                                pos, seq, rec, nch);
-            if (nch > MERGE_W_CHUNKS)   // long contexts: two workgroups per head, 32 dims each
-                hipLaunchKernelGGL((k_attn_merge<64, 2>), mgrid2, dim3(256), 0, s, rec, nq, nch, cap, pos,
-                                   out, o_ts, oq, od);
-            else   // up to 64 chunks (the one-wave merge)
-                hipLaunchKernelGGL(k_attn_merge_w<64>, mgrid, dim3(64), 0, s, rec, nq, nch, cap, pos, out,
-                                   o_ts, oq, od);
+            merge(H{}, C0{});
         }
     } else {
         return QK_ESHAPE;

@@ -362,6 +362,12 @@ ATT_CASES = [
     # long contexts: up to 512 chunks per head in the merge pass
     (2, 32, 4, 64, 32768, 2, "ring"),
     (2, 16, 2, 32, 32768, 2, "ring"),
+    # merge forms by records per head: 65..128 in one wave, two records a
+    # lane (8192 rows); 129..255 on the four-wave merge (12000 rows)
+    (3, 16, 2, 32, 8192, 3, "ring"),
+    (3, 32, 4, 64, 12000, 3, "ring"),
+    (2, 16, 2, 32, 12000, 2, "ring"),
+    (3, 16, 2, 32, 16384, 3, "spread"),   # the long pass's 64 records, head_dim 32
     (40, 32, 4, 64, 16384, 1, "long9k"),  # many tokens past 8192: the tiled pass
     # caches of 256 chunks and more: four chunks per chunk-pass workgroup and
     # record; positions at chunk and four-chunk boundaries give records of
