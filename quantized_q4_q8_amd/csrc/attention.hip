@@ -510,6 +510,78 @@ __global__ __launch_bounds__(64) void k_attn_merge_w(const double* __restrict__ 
     }
 }
 
+// Merge pass for 65..128 records per head, head dim 64: two waves per
+// (head, token), wave z taking dims 32 z .. 32 z + 31, with no workgroup
+// barrier.  Lane c loads the (m, l) of records c and c + 64; lane (half hh,
+// dim d) the values of dim 32 z + d in records 64 hh .. 64 hh + 63.  The
+// max, the record weights and their l-weighted sum are wave reductions; the
+// weights pass through LDS within the wave; each lane adds its 64 records in
+// order and the half holding records 64..127 is added to the other.
+template <int CPW_LOG2>
+__global__ __launch_bounds__(64) void k_attn_merge_w2(const double* __restrict__ rec, int64_t nq,
+                                                      int64_t nch, int64_t cap,
+                                                      const int32_t* __restrict__ pos,
+                                                      float* __restrict__ out, int64_t o_ts,
+                                                      int8_t* __restrict__ oq,
+                                                      uint16_t* __restrict__ od) {
+    constexpr int HD = 64, DH = 32;
+    __shared__ __align__(16) double ws[2 * WAVE];
+    __shared__ __align__(16) float res[DH];
+    const int64_t h = blockIdx.x, t = blockIdx.y;
+    const int z = blockIdx.z;
+    const int lane = threadIdx.x, hh = lane >> 5, d = lane & 31;
+    const int p = pos[t];
+    const bool valid = p >= 0;
+    const int used = valid ? (int)((min((int64_t)p, cap - 1) / ACH) >> CPW_LOG2) + 1 : 0;   // records with rows
+    const double* hr = rec + (t * nq + h) * nch * (HD + 2);
+    const double2 ml0 = *reinterpret_cast<const double2*>(hr + (lane < used ? lane : 0) * (HD + 2));
+    const double2 ml1 = *reinterpret_cast<const double2*>(hr + (lane + WAVE < used ? lane + WAVE : 0) * (HD + 2));
+    double ov[WAVE];
+#pragma unroll
+    for (int c = 0; c < WAVE; ++c) {
+        const int r = hh * WAVE + c;
+        ov[c] = hr[(r < used ? r : 0) * (HD + 2) + 2 + z * DH + d];
+    }
+    double m = lane < used ? ml0.x : -INFINITY;
+    if (lane + WAVE < used) m = fmax(m, ml1.x);
+    const double mx = group_max<WAVE>(m);
+    const double w0 = lane < used ? exp(ml0.x - mx) : 0.0;
+    const double w1 = lane + WAVE < used ? exp(ml1.x - mx) : 0.0;
+    const double ls = group_sum<WAVE>(fma(w1, ml1.y, w0 * ml0.y));
+    ws[lane] = w0;
+    ws[lane + WAVE] = w1;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < WAVE; c += 2) {
+        const double2 wc = *reinterpret_cast<const double2*>(&ws[hh * WAVE + c]);
+        acc = fma(wc.x, ov[c], acc);
+        acc = fma(wc.y, ov[c + 1], acc);
+    }
+    const double other = __shfl_xor(acc, 32, WAVE);
+    const double tot = hh == 0 ? acc + other : other + acc;   // records 0..63, then 64..127
+    const float v = valid ? (float)(tot / ls) : 0.0f;
+    const int64_t col = t * o_ts + h * HD + z * DH;
+    if (out && lane < DH) out[col + lane] = v;
+    if (oq) {
+        if (lane < DH) res[lane] = v;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float vv[8];
+        const int i8 = (lane & 3) * 8;   // lanes 0..3: the block's four quarters
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = res[i8 + e];
+        uint32_t lo, hi;
+        float dd;
+        q8_quad(vv, lo, hi, dd);
+        if (lane < DH / 8) {
+            *reinterpret_cast<uint2*>(oq + col + 8 * lane) = make_uint2(lo, hi);
+            if (lane == 0) od[col / QBLK] = f2h(dd);
+        }
+    }
+}
+
 // Longest-first order of the tiled pass's token tiles (TQ tokens each): a
 // tile's cost is the number of 64-row chunks its furthest position attends,
 // and order[] lists the tiles by cost, largest first (a counting sort; the
@@ -871,18 +943,22 @@ int launch_attention(const float* q, int64_t q_ts, int64_t tokens, int64_t nq, i
     dim3 mgrid((unsigned)nq, (unsigned)tokens);
     dim3 mgrid2((unsigned)nq, (unsigned)tokens, 2u);
     // the merge: one wave per head for up to 64 records per head (4096 rows,
-    // or 16384 with the long pass); more records go to k_attn_merge, whose
-    // four waves (two workgroups for head dim 64) load them faster (a
-    // one-wave form with two records per lane measured slower at 8192 and
-    // 32768 rows)
+    // or 16384 with the long pass); head dim 64 with up to 128 records (the
+    // 8192- and 32768-row rings): two waves per head, 32 dims each; more
+    // records, or head dim 32 past 64: k_attn_merge (a one-wave form with
+    // two records per lane measured slower at 8192 and 32768 rows)
     auto merge = [&](auto hdc, auto cpw) {
         constexpr int HD = decltype(hdc)::value, CPW = decltype(cpw)::value;
         if (nrec <= MERGE_W_CHUNKS) {
             hipLaunchKernelGGL((k_attn_merge_w<HD, CPW>), mgrid, dim3(64), 0, s, rec, nq, nrec, cap, pos,
                                out, o_ts, oq, od);
-        } else if constexpr (HD == 64) {   // two workgroups per head, 32 dims each
-            hipLaunchKernelGGL((k_attn_merge<HD, 2, CPW>), mgrid2, dim3(256), 0, s, rec, nq, nrec, cap, pos,
-                               out, o_ts, oq, od);
+        } else if constexpr (HD == 64) {   // two waves per head, 32 dims each
+            if (nrec <= 2 * MERGE_W_CHUNKS)
+                hipLaunchKernelGGL((k_attn_merge_w2<CPW>), mgrid2, dim3(64), 0, s, rec, nq, nrec, cap, pos,
+                                   out, o_ts, oq, od);
+            else
+                hipLaunchKernelGGL((k_attn_merge<HD, 2, CPW>), mgrid2, dim3(256), 0, s, rec, nq, nrec, cap, pos,
+                                   out, o_ts, oq, od);
         } else {
             hipLaunchKernelGGL((k_attn_merge<HD, 1, CPW>), mgrid, dim3(256), 0, s, rec, nq, nrec, cap, pos,
                                out, o_ts, oq, od);
