@@ -280,17 +280,18 @@ def test_kv_append_bit_exact(gpu_lib):
     assert np.array_equal(host(vcg, np.uint16), vc)
 
 
-@pytest.mark.parametrize("tokens", [6, 13])
-def test_negative_positions_read_and_write_nothing(gpu_lib, tokens):
+@pytest.mark.parametrize("tokens,cap", [(6, 300), (13, 300), (6, 8192)])
+def test_negative_positions_read_and_write_nothing(gpu_lib, tokens, cap):
     """Negative positions (padding tokens) as the header states them: the KV
     store skips their rows and attention gives them zero rows, on the
-    few-token chunk/merge pass (6 tokens) and on the tiled pass (13).  The
-    other tokens equal the oracle over them alone (the oracle takes
-    non-negative positions only; a token's result depends on its own
-    position, sequence and query and on the cache)."""
+    few-token chunk/merge pass (6 tokens: the one-wave merge at 300 rows, the
+    two-wave merge at 8192) and on the tiled pass (13).  The other tokens
+    equal the oracle over them alone (the oracle takes non-negative
+    positions only; a token's result depends on its own position, sequence
+    and query and on the cache)."""
     qk = gpu_lib
-    say(f"negative positions, {tokens} tokens")
-    nq, nkv, hd, cap, seqs = 8, 2, 64, 300, 2
+    say(f"negative positions, {tokens} tokens, cap {cap}")
+    nq, nkv, hd, seqs = 8, 2, 64, 2
     neg = np.arange(tokens) % 3 == 1
     pos = synth.randint(112, 4, tokens, cap).astype(np.int32)
     pos[neg] = -1 - 37 * np.arange(int(neg.sum()), dtype=np.int32)   # -1, -38, ...
