@@ -8,10 +8,15 @@
 // are applied right after it and the scaled block dots are summed in fp64.
 //
 // Tile: a workgroup (4 waves) computes 64 tokens x 128 weight rows; each
-// wave 32 tokens x 64 rows as two MFMA tiles (two workgroups share a CU).  Activations are the MFMA's A
-// operand (rows = tokens) and weights the B operand (columns = weight rows),
-// so in the 32 x 32 accumulator a lane owns one weight row and 16 tokens and
-// the stores of a register are 32 consecutive floats of one output row.
+// wave 32 tokens x 64 rows as two MFMA tiles (two workgroups share a CU).
+// A store-epilogue launch whose grid of such tiles would end on a round of
+// the 512 resident slots that is at most half full (the 4 x 512 prefill's
+// QKV matmul: 640 workgroups) takes 64-row tiles instead, one MFMA tile per
+// wave and three workgroups per CU: prefill 141.2 K -> 142.3 K tokens/s.
+// Activations are the MFMA's A operand (rows = tokens) and weights the B
+// operand (columns = weight rows), so in the 32 x 32 accumulator a lane owns
+// one weight row and 16 tokens and the stores of a register are 32
+// consecutive floats of one output row.
 // KB = 4 blocks (K = 128) are staged in LDS per step, double-buffered so the
 // global loads of step s + 1 are in flight during the MFMAs of step s.  The
 // weight nibbles become signed int8 codes once, while they are staged
@@ -35,15 +40,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BT = 64;   // tokens per workgroup
-constexpr int BR = 128;  // weight rows per workgroup (physical)
 constexpr int KB = 4;    // blocks per LDS stage
 constexpr int NT = 256;  // threads per workgroup: 4 waves, 2 (tokens) x 2 (rows)
 constexpr int STRIDE = KB * QBLK + 16;   // bytes per token / weight row in LDS (padded)
 constexpr int A_PER = BT * KB * 2 / NT;  // 16-byte activation chunks per thread and step
-constexpr int B_PER = BR * KB / NT;      // 16-byte weight chunks per thread and step
-constexpr int DB_PER = BR * KB / NT;     // weight scales per thread and step
 static_assert(BT * KB == NT, "one activation scale per thread and step");
 
+template <int BR>
 struct __align__(16) Stage {
     int8_t a[BT * STRIDE];      // activation codes
     int8_t b[BR * STRIDE];      // weight codes (signed int8)
@@ -67,9 +70,13 @@ __device__ __forceinline__ uint4 nib_codes(const uint4 v, int sh) {
 
 }  // namespace
 
-template <int EPI>
-__global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
-    __shared__ Stage st[2];
+template <int EPI, int WR>
+__global__ __launch_bounds__(NT, WR == 2 ? 2 : 3) void k_gemm_mfma(const GemvArgs a) {
+    static_assert(WR == 2 || (WR == 1 && EPI == EPI_STORE), "SwiGLU tiles hold gate and up rows");
+    constexpr int BR = 64 * WR;          // weight rows per workgroup (physical)
+    constexpr int B_PER = BR * KB / NT;  // 16-byte weight chunks per thread and step
+    constexpr int DB_PER = BR * KB / NT; // weight scales per thread and step
+    __shared__ Stage<BR> st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
             rdbh[i] = wd[rdb_ok[i] ? prow_of(r) * nb + b : 0];
         }
     };
-    auto sstore = [&](Stage& s) {
+    auto sstore = [&](Stage<BR>& s) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int idx = tid + NT * i;
@@ -191,16 +198,16 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
         }
     };
 
-    double acc[2][16];
+    double acc[WR][16];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < WR; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0;
 
     // LDS row (weights) of column tile cb for this wave
     auto lds_col = [&](int cb) -> int {
         if (EPI == EPI_SWIGLU) return cb * (BR / 2) + wc * 32 + j;  // cb 0: gate, 1: up
-        return wc * 64 + cb * 32 + j;
+        return wc * 32 * WR + cb * 32 + j;
     };
     const int tra = wt * 32 + j;   // activation row (token) of this lane's A operand
 
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     sstore(st[0]);
     __syncthreads();
     for (int64_t s = 0; s < nsteps; ++s) {
-        Stage& cur = st[s & 1];
+        Stage<BR>& cur = st[s & 1];
         if (s + 1 < nsteps) gload((s + 1) * KB);
         // two blocks per iteration: the second one's LDS addresses become
         // immediate offsets (1.9 % on the 4 x 512 prefill; a full unroll of
@@ -219,10 +226,10 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
         for (int bb = 0; bb < KB; ++bb) {
             const uint4 av = *reinterpret_cast<const uint4*>(cur.a + tra * STRIDE + bb * QBLK + h * 16);
             const v4i xa = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-            v16i isum[2];
-            double dw[2];
+            v16i isum[WR];
+            double dw[WR];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < WR; ++cb) {
                 const uint4 bv = *reinterpret_cast<const uint4*>(cur.b + lds_col(cb) * STRIDE + bb * QBLK + h * 16);
                 isum[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, v4i{(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w},
                                                                  zero, 0, 0, 0);
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
                 dx[4 * q] = d0.x; dx[4 * q + 1] = d0.y; dx[4 * q + 2] = d1.x; dx[4 * q + 3] = d1.y;
             }
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < WR; ++cb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     acc[cb][v] = fma((double)isum[cb][v] * dx[v], dw[cb], acc[cb][v]);
@@ -252,14 +259,14 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
     // first store: y may equal residual, so the compiler could not move a
     // load above an earlier store, and each load would wait on its own.
     // Every element is read and then written by the same lane.
-    float rv[2][16];
+    float rv[WR][16];
     if (EPI == EPI_STORE && a.residual) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t t = t0 + wt * 32 + 8 * (v / 4) + 4 * h + (v % 4);
             const int64_t tc = cg + (t < m ? t : m - 1);
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < WR; ++cb) {
                 const int pr = lds_col(cb);
                 const int64_t r = prow_valid(pr) ? prow_of(pr) : 0;
                 rv[cb][v] = a.residual[tc * a.ldr + r];
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_mfma(const GemvArgs a) {
         if (t >= m) continue;
         if (EPI == EPI_STORE) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < WR; ++cb) {
                 const int pr = lds_col(cb);
                 if (!prow_valid(pr)) continue;
                 const int64_t r = prow_of(pr);
@@ -294,11 +301,21 @@ int launch_gemm(const GemvArgs& a, int epi, hipStream_t s, int64_t max_group_col
     const unsigned gz = !a.col_off ? 1u : (a.group_list ? (unsigned)max_groups : (unsigned)a.groups);
     if (gt == 0 || gz == 0) return QK_OK;
     if (epi == EPI_SWIGLU) {
+        constexpr int BR = 128;
         dim3 grid((unsigned)((a.ffn + BR / 2 - 1) / (BR / 2)), gt, gz);
-        hipLaunchKernelGGL(k_gemm_mfma<EPI_SWIGLU>, grid, dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_mfma<EPI_SWIGLU, 2>), grid, dim3(NT), 0, s, a);
     } else {
-        dim3 grid((unsigned)((a.n + BR - 1) / BR), gt, gz);
-        hipLaunchKernelGGL(k_gemm_mfma<EPI_STORE>, grid, dim3(NT), 0, s, a);
+        // 128-row tiles, unless their grid would end on a round of the 512
+        // resident slots (two per CU) that is at most half full
+        const int64_t wg2 = (a.n + 127) / 128 * (int64_t)gt * gz;
+        const int64_t tail = wg2 % 512;
+        if (tail > 0 && tail <= 256) {
+            dim3 grid((unsigned)((a.n + 63) / 64), gt, gz);
+            hipLaunchKernelGGL((k_gemm_mfma<EPI_STORE, 1>), grid, dim3(NT), 0, s, a);
+        } else {
+            dim3 grid((unsigned)((a.n + 127) / 128), gt, gz);
+            hipLaunchKernelGGL((k_gemm_mfma<EPI_STORE, 2>), grid, dim3(NT), 0, s, a);
+        }
     }
     return qk_launch_status();
 }
